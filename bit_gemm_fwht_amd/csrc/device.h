@@ -1,0 +1,208 @@
+// Device-side building blocks for gfx950 (CDNA4): bf16 unpacking, DPP lane exchange, the
+// hardware scaled converts to FP4 / FP8, Philox4x32-10, and the scale rules.
+//
+// Everything here is computed in fp32 with IEEE round-to-nearest-even per operation; the library
+// is compiled with -ffp-contract=off so that no multiply-add is fused unless written as fmaf.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bgf {
+
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------------------------
+// bf16 <-> fp32 (bf16 is the top half of an fp32: widening is exact)
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// round-to-nearest-even fp32 -> bf16 bits (inputs are finite)
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------------------------
+// DPP lane exchange within a row of 16 lanes
+// ---------------------------------------------------------------------------------------------
+constexpr int dpp_quad(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// value of lane (lane ^ M), M in {1, 2, 4}
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+    if constexpr (M == 1) return dpp_mov<dpp_quad(1, 0, 3, 2)>(v);
+    if constexpr (M == 2) return dpp_mov<dpp_quad(2, 3, 0, 1)>(v);
+    // xor 4 = mirror within 8 lanes (i -> 7 - i), then reverse within 4 (i -> 3 - i)
+    if constexpr (M == 4) return dpp_mov<dpp_quad(3, 2, 1, 0)>(dpp_mov<DPP_ROW_HALF_MIRROR>(v));
+    return v;
+}
+
+// 1 / sqrt(n) rounded to the nearest fp32, for the Hadamard normalisation
+template <int N>
+__device__ __forceinline__ float inv_sqrt_n() {
+    if constexpr (N == 16) return __uint_as_float(0x3E800000u);   // 0.25
+    if constexpr (N == 32) return __uint_as_float(0x3E3504F3u);   // 0.17677669...
+    if constexpr (N == 64) return __uint_as_float(0x3E000000u);   // 0.125
+    if constexpr (N == 128) return __uint_as_float(0x3DB504F3u);  // 0.08838834...
+    if constexpr (N == 256) return __uint_as_float(0x3D800000u);  // 0.0625
+    return 1.0f;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Hardware converts. The scale operand of the gfx950 scaled converts only contributes its
+// exponent: the result is the conversion of x / 2^floor(log2 scale), computed exactly, rounded to
+// nearest even. FP4 saturates at +-6; FP8 (E4M3) does not saturate, so callers clamp first.
+// ---------------------------------------------------------------------------------------------
+// two fp32 -> two E2M1 nibbles placed in byte SEL of `old`
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b, float scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
+}
+// two fp32 -> two E4M3 bytes in the low (HI = false) or high half of `old`
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt_fp8x2(uint32_t old, float a, float b, float scale) {
+    v2s o;
+    o[0] = (short)(old & 0xFFFF);
+    o[1] = (short)(old >> 16);
+    v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, scale, HI);
+    return ((uint32_t)(uint16_t)r[0]) | ((uint32_t)(uint16_t)r[1] << 16);
+}
+// decode: byte SEL of `src` (two E2M1 nibbles) -> two fp32, exact
+template <int SEL>
+__device__ __forceinline__ v2f fp4x2_to_f32(uint32_t src) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(src, 1.0f, SEL);
+}
+// decode: half HI of `src` (two E4M3 bytes) -> two fp32, exact
+template <bool HI>
+__device__ __forceinline__ v2f fp8x2_to_f32(uint32_t src) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(src, 1.0f, HI);
+}
+
+// E4M3 code of t >= 0, nearest even, saturating at 448 (code 0x7E); NaN -> 0x7E
+__device__ __forceinline__ uint32_t e4m3_code_sat(float t) {
+    if (!(t < 448.0f)) return 0x7Eu;
+    return cvt_fp8x2<false>(0u, t, 0.0f, 1.0f) & 0xFFu;
+}
+// value of a non-negative E4M3 code (0..0x7E)
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9, exact
+    return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// ---------------------------------------------------------------------------------------------
+// Scale rules
+// ---------------------------------------------------------------------------------------------
+// E8M0 exponent k for a block max: floor rule k = floor(log2 amax) - EMAX; ceil (truncation-free)
+// rule: the smallest k with maxval * 2^k >= amax, i.e. one more than the floor rule when the
+// mantissa of amax exceeds that of maxval (1.5 for E2M1, 1.75 for E4M3). Clamped to [-127, 127];
+// amax = 0 gives -127.
+template <int EMAX, uint32_t MAXMANT>
+__device__ __forceinline__ int e8m0_exp(float amax, bool ceil_rule) {
+    uint32_t u = __float_as_uint(amax);
+    if (u == 0u) return -127;
+    int e;
+    uint32_t mant;
+    uint32_t ef = u >> 23;
+    if (ef != 0u) {
+        e = (int)ef - 127;
+        mant = u & 0x7FFFFFu;
+    } else {  // subnormal amax
+        int p = 31 - __clz(u);
+        e = p - 149;
+        mant = (u << (23 - p)) & 0x7FFFFFu;
+    }
+    int k = e - EMAX + ((ceil_rule && mant > MAXMANT) ? 1 : 0);
+    return k < -127 ? -127 : (k > 127 ? 127 : k);
+}
+
+// 2^k as an fp32 for k in [-126, 127]
+__device__ __forceinline__ float pow2f(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
+
+// reciprocal of a scale: 0 -> 0, an overflowing reciprocal -> FLT_MAX
+__device__ __forceinline__ float scale_recip(float d) {
+    if (d == 0.0f) return 0.0f;
+    float r = 1.0f / d;
+    return (__float_as_uint(r) & 0x7FFFFFFFu) == 0x7F800000u ? 3.40282347e38f : r;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., SC'11): 10 rounds of two 32x32->64 multiplies and a key schedule
+// advanced by the Weyl constants.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2,
+                                              uint32_t& c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Stochastic rounding: between the grid neighbours lo <= |v| < hi, round up iff u < p * 2^16,
+// p = (|v| - lo) / (hi - lo) (exact: the gap is a power of two). Saturates at the grid maximum.
+// Returns the code (sign bit 3 for E2M1, bit 7 for E4M3).
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t u16) {
+    const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
+    const float a = fabsf(v);
+    if (!(a < 6.0f)) return sign | 7u;
+    uint32_t lo;
+    float p;
+    if (a >= 1.0f) {
+        // a in [1, 6): grid spacing within binade e (0, 1, 2) is 2^(e-1); lo keeps 1 mantissa bit
+        const uint32_t ua = __float_as_uint(a);
+        const uint32_t e = (ua >> 23) - 127u;
+        const float glo = __uint_as_float(ua & 0xFFC00000u);
+        lo = 2u + 2u * e + ((ua >> 22) & 1u);
+        p = (a - glo) * __uint_as_float((128u - e) << 23);  // / 2^(e-1)
+    } else {
+        lo = a >= 0.5f ? 1u : 0u;
+        p = (a - 0.5f * (float)lo) * 2.0f;
+    }
+    const uint32_t up = ((float)u16 < p * 65536.0f) ? 1u : 0u;
+    return sign | (lo + up);
+}
+
+__device__ __forceinline__ uint32_t e4m3_sr(float v, uint32_t u16) {
+    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    const float a = fabsf(v);
+    if (!(a < 448.0f)) return sign | 0x7Eu;
+    uint32_t lo;
+    float p;
+    const uint32_t ua = __float_as_uint(a);
+    if (a >= 0.015625f) {  // normal E4M3 range: keep 3 mantissa bits
+        const uint32_t e = (ua >> 23);          // biased fp32 exponent, 121..135
+        const float glo = __uint_as_float(ua & 0xFFF00000u);
+        lo = ((e - 120u) << 3) | ((ua >> 20) & 7u);
+        p = (a - glo) * __uint_as_float((130u - (e - 127u)) << 23);  // / 2^(e-127-3)
+    } else {  // subnormal E4M3: step 2^-9
+        const float q = floorf(a * 512.0f);
+        lo = (uint32_t)q;
+        p = a * 512.0f - q;
+    }
+    const uint32_t up = ((float)u16 < p * 65536.0f) ? 1u : 0u;
+    return sign | (lo + up);
+}
+
+}  // namespace bgf

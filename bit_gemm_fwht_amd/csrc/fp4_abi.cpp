@@ -1,0 +1,338 @@
+// C ABI of libbgf (declared in include/fp4.h): host-side validation, size queries and dispatch to
+// the HIP kernels. Nothing is queued unless every argument has been accepted.
+#include "../../include/fp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fp4_internal.h"
+
+namespace {
+
+using namespace bgf;
+
+enum Layout { L_BAD = 0, L_SEG1D, L_SEG2D, L_ROW, L_TENSOR };
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool valid_hn(int n) { return n == 0 || n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
+
+bool is_nv(int sm) { return sm == FP4_SCALE_NV || sm == FP4_SCALE_NV_4OVER6; }
+
+int scale_class(int sm) {
+    if (sm == FP4_SCALE_E8M0_FLOOR || sm == FP4_SCALE_E8M0_CEIL) return SC_E8M0;
+    if (is_nv(sm)) return SC_NV;
+    return SC_F32;
+}
+
+// Classify and validate a (rows, cols, params) triple; returns FP4_OK and the layout.
+int check_params(int64_t rows, int64_t cols, const fp4_qparams* p, Layout* lay) {
+    *lay = L_BAD;
+    if (!p || rows <= 0 || cols <= 0) return FP4_ERR_INVALID_ARG;
+    if (p->elem != FP4_ELEM_E2M1 && p->elem != FP4_ELEM_E4M3) return FP4_ERR_INVALID_ARG;
+    if (p->scale_mode < FP4_SCALE_E8M0_FLOOR || p->scale_mode > FP4_SCALE_F32) return FP4_ERR_INVALID_ARG;
+    if (p->round_mode != FP4_ROUND_RNE && p->round_mode != FP4_ROUND_SR) return FP4_ERR_INVALID_ARG;
+    if (p->block_rows <= 0 || p->block_cols <= 0) return FP4_ERR_INVALID_ARG;
+    if (rows % p->block_rows || cols % p->block_cols) return FP4_ERR_INVALID_ARG;
+    if (p->elem == FP4_ELEM_E2M1 && (cols & 1)) return FP4_ERR_INVALID_ARG;
+    if (!valid_hn(p->hadamard_n)) return FP4_ERR_INVALID_ARG;
+    if (p->hadamard_n && cols % p->hadamard_n) return FP4_ERR_INVALID_ARG;
+    const int br = p->block_rows, bc = p->block_cols;
+    if (br == 1 && (bc == 16 || bc == 32) && cols % 32 == 0) *lay = L_SEG1D;
+    else if (br == 32 && bc == 32 && cols % 32 == 0) *lay = L_SEG2D;
+    else if (br == 1 && bc == cols) *lay = L_ROW;
+    else if (br == rows && bc == cols) *lay = L_TENSOR;
+    else return FP4_ERR_UNSUPPORTED;
+    if (is_nv(p->scale_mode)) {
+        if (p->elem != FP4_ELEM_E2M1 || *lay != L_SEG1D || bc != 16) return FP4_ERR_UNSUPPORTED;
+        if (p->scale_mode == FP4_SCALE_NV_4OVER6 && p->round_mode == FP4_ROUND_SR) return FP4_ERR_UNSUPPORTED;
+    }
+    if (*lay == L_SEG2D && scale_class(p->scale_mode) != SC_E8M0) return FP4_ERR_UNSUPPORTED;
+    if ((*lay == L_ROW || *lay == L_TENSOR) && p->hadamard_n) return FP4_ERR_UNSUPPORTED;
+    return FP4_OK;
+}
+
+int64_t codes_bytes(int64_t rows, int64_t cols, const fp4_qparams* p) {
+    return p->elem == FP4_ELEM_E2M1 ? rows * (cols / 2) : rows * cols;
+}
+int64_t scales_bytes(int64_t rows, int64_t cols, const fp4_qparams* p) {
+    const int64_t n = (rows / p->block_rows) * (cols / p->block_cols);
+    return scale_class(p->scale_mode) == SC_F32 ? 4 * n : n;
+}
+int64_t ws_bytes_needed(Layout lay, const fp4_qparams* p) {
+    return (is_nv(p->scale_mode) || lay == L_TENSOR) ? 256 : 0;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fp4_abi_version(void) { return FP4_ABI_VERSION; }
+
+const char* fp4_status_string(int s) {
+    switch (s) {
+        case FP4_OK: return "ok";
+        case FP4_ERR_INVALID_ARG: return "invalid argument";
+        case FP4_ERR_UNSUPPORTED: return "unsupported combination";
+        case FP4_ERR_ALIGNMENT: return "misaligned pointer or pitch (16 bytes required)";
+        case FP4_ERR_WORKSPACE: return "workspace missing or too small";
+        case FP4_ERR_HIP: return "HIP runtime error";
+        case FP4_ERR_INTERNAL: return "internal error";
+        default: return "unknown status";
+    }
+}
+
+int64_t fp4_codes_bytes(int64_t rows, int64_t cols, const fp4_qparams* p) {
+    Layout lay;
+    if (check_params(rows, cols, p, &lay) != FP4_OK) return -1;
+    return codes_bytes(rows, cols, p);
+}
+
+int64_t fp4_scales_bytes(int64_t rows, int64_t cols, const fp4_qparams* p) {
+    Layout lay;
+    if (check_params(rows, cols, p, &lay) != FP4_OK) return -1;
+    return scales_bytes(rows, cols, p);
+}
+
+int64_t fp4_workspace_bytes(int64_t rows, int64_t cols, const fp4_qparams* p) {
+    Layout lay;
+    if (check_params(rows, cols, p, &lay) != FP4_OK) return -1;
+    return ws_bytes_needed(lay, p);
+}
+
+int fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                 const fp4_qparams* p, void* codes, void* scales, float* tensor_scale,
+                 void* workspace, int64_t ws_bytes, void* stream) {
+    try {
+        Layout lay;
+        int rc = check_params(rows, cols, p, &lay);
+        if (rc != FP4_OK) return rc;
+        if (!x || !codes || !scales) return FP4_ERR_INVALID_ARG;
+        if (x_dtype != FP4_DT_F32 && x_dtype != FP4_DT_BF16) return FP4_ERR_INVALID_ARG;
+        if (ldx < cols) return FP4_ERR_INVALID_ARG;
+        if (codes == x || scales == x || codes == scales) return FP4_ERR_INVALID_ARG;
+        if (is_nv(p->scale_mode) && !tensor_scale) return FP4_ERR_INVALID_ARG;
+        const int esz = x_dtype == FP4_DT_BF16 ? 2 : 4;
+        if (lay == L_SEG1D || lay == L_SEG2D) {
+            if (!aligned(x, 16) || (ldx * esz) % 16 || !aligned(codes, 16) || !aligned(scales, 8))
+                return FP4_ERR_ALIGNMENT;
+        }
+        const int64_t need = ws_bytes_needed(lay, p);
+        if (need && (!workspace || ws_bytes < need)) return FP4_ERR_WORKSPACE;
+        if (need && !aligned(workspace, 4)) return FP4_ERR_ALIGNMENT;
+
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        const int sc = scale_class(p->scale_mode);
+        uint32_t* ws = reinterpret_cast<uint32_t*>(workspace);
+        if (lay == L_SEG1D || lay == L_SEG2D) {
+            SegArgs a{};
+            a.x = x;
+            a.rows = rows;
+            a.cols = cols;
+            a.ldx = ldx;
+            a.nseg = rows * (cols / 32);
+            a.codes = reinterpret_cast<uint8_t*>(codes);
+            a.scales = scales;
+            a.tensor_scale = tensor_scale;
+            a.ws = ws;
+            a.seed = p->seed;
+            a.ceil_rule = p->scale_mode == FP4_SCALE_E8M0_CEIL;
+            a.four_six = p->scale_mode == FP4_SCALE_NV_4OVER6;
+            if (sc == SC_NV) {
+                if ((rc = hip_status(launch_zero_u32(ws, 1, s))) != FP4_OK) return rc;
+                rc = hip_status(launch_segment(a, x_dtype, p->hadamard_n, p->elem, sc, p->round_mode, 1,
+                                               32, PASS_AMAX, s));
+                if (rc != FP4_OK) return rc;
+            }
+            return hip_status(launch_segment(a, x_dtype, p->hadamard_n, p->elem, sc, p->round_mode,
+                                             p->block_rows, p->block_cols, PASS_QUANT, s));
+        }
+        RowArgs a{};
+        a.x = x;
+        a.rows = rows;
+        a.cols = cols;
+        a.ldx = ldx;
+        a.codes = reinterpret_cast<uint8_t*>(codes);
+        a.scales = scales;
+        a.ws = ws;
+        a.seed = p->seed;
+        a.ceil_rule = p->scale_mode == FP4_SCALE_E8M0_CEIL;
+        a.per_tensor = lay == L_TENSOR;
+        if (lay == L_TENSOR) {
+            if ((rc = hip_status(launch_zero_u32(ws, 1, s))) != FP4_OK) return rc;
+            if ((rc = hip_status(launch_amax_rows(x, x_dtype, rows, cols, ldx, ws, s))) != FP4_OK) return rc;
+        }
+        return hip_status(launch_rowblock(a, x_dtype, p->elem, sc, p->round_mode, s));
+    } catch (...) {
+        return FP4_ERR_INTERNAL;
+    }
+}
+
+int fp4_dequantize(const void* codes, const void* scales, const float* tensor_scale, int64_t rows,
+                   int64_t cols, const fp4_qparams* p, void* y, int32_t y_dtype, int64_t ldy,
+                   void* stream) {
+    try {
+        Layout lay;
+        int rc = check_params(rows, cols, p, &lay);
+        if (rc != FP4_OK) return rc;
+        if (!codes || !scales || !y) return FP4_ERR_INVALID_ARG;
+        if (y_dtype != FP4_DT_F32 && y_dtype != FP4_DT_BF16) return FP4_ERR_INVALID_ARG;
+        if (ldy < cols) return FP4_ERR_INVALID_ARG;
+        if (is_nv(p->scale_mode) && !tensor_scale) return FP4_ERR_INVALID_ARG;
+        const int esz = y_dtype == FP4_DT_BF16 ? 2 : 4;
+        if (lay == L_SEG1D || lay == L_SEG2D) {
+            if (!aligned(y, 16) || (ldy * esz) % 16 || !aligned(codes, 16) || !aligned(scales, 8))
+                return FP4_ERR_ALIGNMENT;
+        }
+        DeqArgs a{};
+        a.codes = reinterpret_cast<const uint8_t*>(codes);
+        a.scales = scales;
+        a.tensor_scale = tensor_scale;
+        a.rows = rows;
+        a.cols = cols;
+        a.nseg = rows * (cols / 32);
+        a.y = y;
+        a.ldy = ldy;
+        a.per_tensor = lay == L_TENSOR;
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        const int sc = scale_class(p->scale_mode);
+        if (lay == L_SEG1D || lay == L_SEG2D)
+            return hip_status(launch_dequant_segment(a, p->elem, sc, p->block_rows, p->block_cols,
+                                                     p->hadamard_n, y_dtype, s));
+        return hip_status(launch_dequant_rowblock(a, p->elem, sc, y_dtype, s));
+    } catch (...) {
+        return FP4_ERR_INTERNAL;
+    }
+}
+
+int fp4_hadamard(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                 int32_t hadamard_n, float* y, void* stream) {
+    try {
+        if (!x || !y || rows <= 0 || cols <= 0 || ldx < cols) return FP4_ERR_INVALID_ARG;
+        if (x_dtype != FP4_DT_F32 && x_dtype != FP4_DT_BF16) return FP4_ERR_INVALID_ARG;
+        if (!valid_hn(hadamard_n) || cols % 32 || (hadamard_n && cols % hadamard_n)) return FP4_ERR_INVALID_ARG;
+        const int esz = x_dtype == FP4_DT_BF16 ? 2 : 4;
+        if (!aligned(x, 16) || (ldx * esz) % 16 || !aligned(y, 16)) return FP4_ERR_ALIGNMENT;
+        SegArgs a{};
+        a.x = x;
+        a.rows = rows;
+        a.cols = cols;
+        a.ldx = ldx;
+        a.nseg = rows * (cols / 32);
+        a.yrot = y;
+        return hip_status(launch_segment(a, x_dtype, hadamard_n, FP4_ELEM_E2M1, SC_E8M0, FP4_ROUND_RNE,
+                                         1, 32, PASS_ROTATE, reinterpret_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return FP4_ERR_INTERNAL;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// GEMM
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+// 0 MXFP4, 1 MXFP8, 2 NVFP4; -1 unsupported
+int gemm_kind(const fp4_qtensor* A, const fp4_qtensor* B, int* b2d) {
+    const fp4_qparams &pa = A->p, &pb = B->p;
+    *b2d = 0;
+    if (pa.elem != pb.elem) return -1;
+    const bool a_mx = scale_class(pa.scale_mode) == SC_E8M0 && pa.block_rows == 1 && pa.block_cols == 32;
+    const bool b_mx = scale_class(pb.scale_mode) == SC_E8M0 && pb.block_rows == 1 && pb.block_cols == 32;
+    const bool b_2d = scale_class(pb.scale_mode) == SC_E8M0 && pb.block_rows == 32 && pb.block_cols == 32;
+    if (pa.elem == FP4_ELEM_E2M1 && a_mx && (b_mx || b_2d)) {
+        *b2d = b_2d;
+        return 0;
+    }
+    if (pa.elem == FP4_ELEM_E4M3 && a_mx && b_mx) return 1;
+    const bool a_nv = is_nv(pa.scale_mode) && pa.block_rows == 1 && pa.block_cols == 16;
+    const bool b_nv = is_nv(pb.scale_mode) && pb.block_rows == 1 && pb.block_cols == 16;
+    if (pa.elem == FP4_ELEM_E2M1 && a_nv && b_nv) return 2;
+    return -1;
+}
+
+int64_t gemm_ws(const fp4_qtensor* A, const fp4_qtensor* B, int kind) {
+    if (kind != 2) return 0;
+    auto r = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const int64_t K = A->cols;
+    return r(A->rows * K) + r(A->rows * K / 32) + r(B->rows * K) + r(B->rows * K / 32);
+}
+
+int check_operand(const fp4_qtensor* T) {
+    Layout lay;
+    int rc = check_params(T->rows, T->cols, &T->p, &lay);
+    if (rc != FP4_OK) return rc;
+    if (!T->codes || !T->scales) return FP4_ERR_INVALID_ARG;
+    if (!aligned(T->codes, 16) || !aligned(T->scales, 4)) return FP4_ERR_ALIGNMENT;
+    if (is_nv(T->p.scale_mode) && !T->tensor_scale) return FP4_ERR_INVALID_ARG;
+    return FP4_OK;
+}
+
+}  // namespace
+
+int64_t fp4_gemm_workspace_bytes(const fp4_qtensor* A, const fp4_qtensor* B) {
+    if (!A || !B || check_operand(A) != FP4_OK || check_operand(B) != FP4_OK) return -1;
+    int b2d;
+    const int kind = gemm_kind(A, B, &b2d);
+    if (kind < 0) return -1;
+    return gemm_ws(A, B, kind);
+}
+
+int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtype, int64_t ldc,
+             const fp4_qparams* out_q, fp4_qtensor* C_q, void* workspace, int64_t ws_bytes,
+             void* stream) {
+    try {
+        if (!A || !B) return FP4_ERR_INVALID_ARG;
+        int rc;
+        if ((rc = check_operand(A)) != FP4_OK) return rc;
+        if ((rc = check_operand(B)) != FP4_OK) return rc;
+        if (A->cols != B->cols) return FP4_ERR_INVALID_ARG;
+        const int64_t M = A->rows, N = B->rows, K = A->cols;
+        if (K % 128) return FP4_ERR_UNSUPPORTED;
+        if (A->p.hadamard_n != B->p.hadamard_n) return FP4_ERR_INVALID_ARG;
+        int b2d;
+        const int kind = gemm_kind(A, B, &b2d);
+        if (kind < 0) return FP4_ERR_UNSUPPORTED;
+        if (out_q || C_q) return FP4_ERR_UNSUPPORTED;  // fused output quantization: not built yet
+        if (!C) return FP4_ERR_INVALID_ARG;
+        if (c_dtype != FP4_DT_F32 && c_dtype != FP4_DT_BF16) return FP4_ERR_INVALID_ARG;
+        if (ldc < N) return FP4_ERR_INVALID_ARG;
+        if (!aligned(C, 16)) return FP4_ERR_ALIGNMENT;
+        const int64_t need = gemm_ws(A, B, kind);
+        if (need && (!workspace || ws_bytes < need)) return FP4_ERR_WORKSPACE;
+        if (need && !aligned(workspace, 256)) return FP4_ERR_ALIGNMENT;
+
+        GemmArgs g{};
+        g.a = reinterpret_cast<const uint8_t*>(A->codes);
+        g.b = reinterpret_cast<const uint8_t*>(B->codes);
+        g.sa = reinterpret_cast<const uint8_t*>(A->scales);
+        g.sb = reinterpret_cast<const uint8_t*>(B->scales);
+        g.ga = A->tensor_scale;
+        g.gb = B->tensor_scale;
+        g.M = M;
+        g.N = N;
+        g.K = K;
+        g.c = C;
+        g.ldc = ldc;
+        g.b_2d = b2d;
+        if (kind == 2) {
+            auto r = [](int64_t x) { return (x + 255) / 256 * 256; };
+            uint8_t* w = reinterpret_cast<uint8_t*>(workspace);
+            g.a8 = w;
+            w += r(M * K);
+            g.sa8 = w;
+            w += r(M * K / 32);
+            g.b8 = w;
+            w += r(N * K);
+            g.sb8 = w;
+        }
+        return hip_status(launch_gemm(g, kind, c_dtype, 0, reinterpret_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return FP4_ERR_INTERNAL;
+    }
+}
+
+}  // extern "C"

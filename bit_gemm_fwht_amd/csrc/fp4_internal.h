@@ -1,0 +1,87 @@
+// Internal interfaces between the C ABI (fp4_abi.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bgf {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+enum { ELEM_E2M1 = 0, ELEM_E4M3 = 1 };
+enum { SC_E8M0 = 0, SC_NV = 1, SC_F32 = 2 };  // scale classes (floor/ceil and 4/6 are runtime)
+enum { RND_RNE = 0, RND_SR = 1 };
+enum { PASS_QUANT = 0, PASS_AMAX = 1, PASS_ROTATE = 2 };
+
+struct SegArgs {
+    const void* x;
+    int64_t rows, cols, ldx;
+    int64_t nseg;          // rows * cols / 32
+    uint8_t* codes;
+    void* scales;
+    float* tensor_scale;   // NV: receives g
+    uint32_t* ws;          // tensor amax (fp32 bits), NV modes
+    float* yrot;           // rotation pass output [rows, cols] fp32
+    uint64_t seed;
+    int ceil_rule;
+    int four_six;
+};
+
+struct RowArgs {
+    const void* x;
+    int64_t rows, cols, ldx;
+    uint8_t* codes;
+    void* scales;
+    uint32_t* ws;
+    uint64_t seed;
+    int ceil_rule;
+    int per_tensor;
+};
+
+struct DeqArgs {
+    const uint8_t* codes;
+    const void* scales;
+    const float* tensor_scale;
+    int64_t rows, cols, nseg;
+    void* y;
+    int64_t ldy;
+    int per_tensor;
+};
+
+hipError_t launch_segment(const SegArgs& a, int in_dtype, int hn, int elem, int sc, int rnd, int br,
+                          int bc, int pass, hipStream_t s);
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
+hipError_t launch_amax_rows(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                            uint32_t* ws, hipStream_t s);
+hipError_t launch_rowblock(const RowArgs& a, int in_dtype, int elem, int sc, int rnd, hipStream_t s);
+hipError_t launch_dequant_segment(const DeqArgs& a, int elem, int sc, int br, int bc, int hn,
+                                  int out_dtype, hipStream_t s);
+hipError_t launch_dequant_rowblock(const DeqArgs& a, int elem, int sc, int out_dtype, hipStream_t s);
+
+// GEMM
+struct GemmArgs {
+    const uint8_t* a;        // [M, K/2] (E2M1) or [M, K] (E4M3)
+    const uint8_t* b;        // [N, K/2] or [N, K]
+    const uint8_t* sa;       // [M, K/32] E8M0, or [M, K/16] E4M3 (NV)
+    const uint8_t* sb;       // [N, K/32], [N/32, K/32] (2D), or [N, K/16] (NV)
+    const float* ga;         // NV tensor scales
+    const float* gb;
+    int64_t M, N, K;
+    void* c;
+    int64_t ldc;
+    int b_2d;
+    // fused output quantization along N (MX groups of 32)
+    uint8_t* qcodes;
+    uint8_t* qscales;
+    int q_elem, q_ceil, q_round;
+    uint64_t q_seed;
+    // NV operands re-expressed as MXFP8 (workspace)
+    uint8_t* a8;
+    uint8_t* sa8;
+    uint8_t* b8;
+    uint8_t* sb8;
+};
+
+// kind: 0 MXFP4, 1 MXFP8, 2 NVFP4 (via the FP8 rescale)
+hipError_t launch_gemm(const GemmArgs& g, int kind, int c_dtype, int fused_q, hipStream_t s);
+
+}  // namespace bgf

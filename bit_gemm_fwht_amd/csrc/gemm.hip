@@ -1,0 +1,245 @@
+// Block-scaled GEMM C = A * B^T on gfx950's V_MFMA_SCALE_F32_16X16X128_F8F6F4.
+//
+// Operands are K-contiguous: A [M, K] and B [N, K] as packed E2M1 (2 per byte) or E4M3 bytes,
+// with one E8M0 scale per row and 32-wide K group (B may instead carry one scale per 32 x 32
+// tile). The matrix core applies both scales itself, so the main loop is loads + MFMA only.
+//
+// Lane layouts of the 16x16x128 scaled MFMA (established with one-hot probes on the hardware):
+//  - FP4: lane l supplies row l % 16 and the 32 K values [32 (l / 16), +32) as 16 contiguous
+//    bytes; FP8: the same row, K values [16 (l / 16), +16) and [64 + 16 (l / 16), +16) as two
+//    16-byte pieces. In both, lane l's scale byte belongs to row l % 16, K group l / 16.
+//  - result: lane l holds D[4 (l / 16) + i][l % 16], i = 0..3, for D = opA * opB^T.
+// The kernel feeds B tiles as opA and A tiles as opB, so each lane ends up with 4 consecutive
+// columns n of one output row m and writes them with one vector store.
+//
+// Tiling: a 256-thread workgroup computes a 128 x 128 block of C; its 4 waves each own a 64 x 64
+// quadrant (4 x 4 MFMA tiles, 64 accumulator registers). Each 128-deep K step stages the A and B
+// slabs (64 B or 128 B per row, rows padded by 16 B so that the 16-byte fragment reads of
+// consecutive rows fall in different LDS banks) and the scale dwords through LDS; the next step's
+// global loads are issued before the current step's MFMAs.
+//
+// NVFP4 operands (16-element blocks with E4M3 scales and an fp32 tensor scale) are first
+// re-expressed as E4M3 elements with one power-of-two scale per 32-wide K group, the form the
+// matrix core takes: per group, with S the larger of its two block scales, E is the smallest
+// exponent with 448 * 2^E >= 6 S and every element becomes E4M3(val(q) * s_blk * 2^-E) (nearest
+// even). The MXFP8 product is then scaled by RN(g_A * g_B) in the epilogue.
+#include "device.h"
+#include "fp4_internal.h"
+
+namespace bgf {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 128, BN = 128, BK = 128, NT = 256;
+
+template <bool FP8>
+struct Cfg {
+    static constexpr int RB = FP8 ? 128 : 64;      // bytes per row per K step
+    static constexpr int LD = RB + 16;             // padded LDS row pitch
+    static constexpr int CH = RB / 16;             // 16-byte chunks per row
+    static constexpr int LOADS = BM * CH / NT;     // 16-byte loads per thread per operand
+};
+
+template <bool FP8, bool B2D, int OUT, bool NVG>
+__global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
+    using C = Cfg<FP8>;
+    __shared__ __attribute__((aligned(16))) uint8_t sA[BM * C::LD];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[BN * C::LD];
+    __shared__ uint32_t sSA[BM], sSB[BN];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+    const int64_t rowbytes = FP8 ? g.K : g.K / 2;
+    const int64_t kgroups = g.K / 32;
+    const int KT = (int)(g.K / BK);
+
+    uint4 ra[C::LOADS], rb[C::LOADS];
+    uint32_t rsa = 0, rsb = 0;
+
+    auto gload = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i) {
+            const int ch = tid + NT * i, r = ch / C::CH, c = ch % C::CH;
+            const int64_t m = m0 + r, n = n0 + r;
+            const int64_t off = (int64_t)kt * C::RB + 16 * c;
+            ra[i] = m < g.M ? *reinterpret_cast<const uint4*>(g.a + m * rowbytes + off) : make_uint4(0, 0, 0, 0);
+            rb[i] = n < g.N ? *reinterpret_cast<const uint4*>(g.b + n * rowbytes + off) : make_uint4(0, 0, 0, 0);
+        }
+        if (tid < BM) {
+            const int64_t m = m0 + tid;
+            rsa = m < g.M ? *reinterpret_cast<const uint32_t*>(g.sa + m * kgroups + 4 * kt) : 0u;
+        } else {
+            const int64_t n = n0 + (tid - BM);
+            if (n < g.N) {
+                const int64_t srow = B2D ? (n >> 5) : n;
+                rsb = *reinterpret_cast<const uint32_t*>(g.sb + srow * kgroups + 4 * kt);
+            } else {
+                rsb = 0u;
+            }
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i) {
+            const int ch = tid + NT * i, r = ch / C::CH, c = ch % C::CH;
+            *reinterpret_cast<uint4*>(sA + r * C::LD + 16 * c) = ra[i];
+            *reinterpret_cast<uint4*>(sB + r * C::LD + 16 * c) = rb[i];
+        }
+        if (tid < BM) sSA[tid] = rsa;
+        else sSB[tid - BM] = rsb;
+    };
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int fr = lane & 15, fg = lane >> 4;
+    gload(0);
+    for (int kt = 0; kt < KT; ++kt) {
+        __syncthreads();
+        lstore();
+        __syncthreads();
+        if (kt + 1 < KT) gload(kt + 1);
+
+        v8i fa[4], fb[4];
+        int sa_[4], sb_[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ra_ = wm * 64 + 16 * i + fr;  // A tile row (output m)
+            const int rb_ = wn * 64 + 16 * i + fr;  // B tile row (output n)
+            if constexpr (!FP8) {
+                const uint4 xa = *reinterpret_cast<const uint4*>(sA + ra_ * C::LD + 16 * fg);
+                const uint4 xb = *reinterpret_cast<const uint4*>(sB + rb_ * C::LD + 16 * fg);
+                fa[i] = (v8i){(int)xa.x, (int)xa.y, (int)xa.z, (int)xa.w, 0, 0, 0, 0};
+                fb[i] = (v8i){(int)xb.x, (int)xb.y, (int)xb.z, (int)xb.w, 0, 0, 0, 0};
+            } else {
+                const uint4 xa0 = *reinterpret_cast<const uint4*>(sA + ra_ * C::LD + 16 * fg);
+                const uint4 xa1 = *reinterpret_cast<const uint4*>(sA + ra_ * C::LD + 64 + 16 * fg);
+                const uint4 xb0 = *reinterpret_cast<const uint4*>(sB + rb_ * C::LD + 16 * fg);
+                const uint4 xb1 = *reinterpret_cast<const uint4*>(sB + rb_ * C::LD + 64 + 16 * fg);
+                fa[i] = (v8i){(int)xa0.x, (int)xa0.y, (int)xa0.z, (int)xa0.w,
+                              (int)xa1.x, (int)xa1.y, (int)xa1.z, (int)xa1.w};
+                fb[i] = (v8i){(int)xb0.x, (int)xb0.y, (int)xb0.z, (int)xb0.w,
+                              (int)xb1.x, (int)xb1.y, (int)xb1.z, (int)xb1.w};
+            }
+            sa_[i] = (int)((sSA[ra_] >> (8 * fg)) & 0xFFu);
+            sb_[i] = (int)((sSB[rb_] >> (8 * fg)) & 0xFFu);
+        }
+#pragma unroll
+        for (int in = 0; in < 4; ++in)
+#pragma unroll
+            for (int im = 0; im < 4; ++im)
+                acc[in][im] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    fb[in], fa[im], acc[in][im], FP8 ? 0 : 4, FP8 ? 0 : 4, 0, sb_[in], 0, sa_[im]);
+    }
+
+    // epilogue: lane holds C[m][n .. n+3]
+    float gscale = 1.0f;
+    if constexpr (NVG) gscale = (*g.ga) * (*g.gb);
+#pragma unroll
+    for (int in = 0; in < 4; ++in)
+#pragma unroll
+        for (int im = 0; im < 4; ++im) {
+            const int64_t m = m0 + wm * 64 + 16 * im + fr;
+            const int64_t n = n0 + wn * 64 + 16 * in + 4 * fg;
+            if (m >= g.M) continue;
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = NVG ? acc[in][im][i] * gscale : acc[in][im][i];
+            if constexpr (OUT == DT_F32) {
+                float* cp = reinterpret_cast<float*>(g.c) + m * g.ldc + n;
+                if (n + 3 < g.N && ((g.ldc & 3) == 0)) {
+                    *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (n + i < g.N) cp[i] = v[i];
+                }
+            } else {
+                uint16_t* cp = reinterpret_cast<uint16_t*>(g.c) + m * g.ldc + n;
+                const uint32_t w0 = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
+                const uint32_t w1 = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+                if (n + 3 < g.N && ((g.ldc & 3) == 0)) {
+                    *reinterpret_cast<uint2*>(cp) = make_uint2(w0, w1);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (n + i < g.N) cp[i] = (uint16_t)bf16_rne_bits(v[i]);
+                }
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------------------------
+// NVFP4 -> MXFP8 re-expression: one lane per 32-wide K group of one row.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_nv_to_fp8(const uint8_t* codes, const uint8_t* scales,
+                                                   int64_t rows, int64_t K, uint8_t* out,
+                                                   uint8_t* out_scales) {
+    const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t groups = rows * (K / 32);
+    if (gi >= groups) return;
+    const uint4 q = *reinterpret_cast<const uint4*>(codes + gi * 16);
+    const uint32_t s01 = *reinterpret_cast<const uint16_t*>(scales + gi * 2);
+    const float s0 = e4m3_value(s01 & 0x7Fu), s1 = e4m3_value((s01 >> 8) & 0x7Fu);
+    const float S = fmaxf(s0, s1);
+    // E = smallest exponent with 448 * 2^E >= 6 S (6 S is exact in fp32)
+    const int E = e8m0_exp<8, 0x600000u>(6.0f * S, true);
+    out_scales[gi] = (uint8_t)(E + 127);
+    const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+    uint32_t o[8];
+    const float sc = E > -127 ? pow2f(E) : 1.0f;  // S = 0: every product is 0
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float sb = w < 2 ? s0 : s1;
+        const v2f p0 = fp4x2_to_f32<0>(qw[w]), p1 = fp4x2_to_f32<1>(qw[w]);
+        const v2f p2 = fp4x2_to_f32<2>(qw[w]), p3 = fp4x2_to_f32<3>(qw[w]);
+        uint32_t r0 = 0u, r1 = 0u;
+        r0 = cvt_fp8x2<false>(r0, p0[0] * sb, p0[1] * sb, sc);
+        r0 = cvt_fp8x2<true>(r0, p1[0] * sb, p1[1] * sb, sc);
+        r1 = cvt_fp8x2<false>(r1, p2[0] * sb, p2[1] * sb, sc);
+        r1 = cvt_fp8x2<true>(r1, p3[0] * sb, p3[1] * sb, sc);
+        o[2 * w] = r0;
+        o[2 * w + 1] = r1;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(out + gi * 32);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+template <bool FP8, bool B2D, bool NVG>
+static hipError_t launch_out(const GemmArgs& g, int c_dtype, hipStream_t s) {
+    dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM));
+    if (c_dtype == DT_BF16) hipLaunchKernelGGL((k_gemm<FP8, B2D, DT_BF16, NVG>), grid, dim3(NT), 0, s, g);
+    else hipLaunchKernelGGL((k_gemm<FP8, B2D, DT_F32, NVG>), grid, dim3(NT), 0, s, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& g, int kind, int c_dtype, int fused_q, hipStream_t s) {
+    (void)fused_q;
+    if (kind == 0) {
+        if (g.b_2d) return launch_out<false, true, false>(g, c_dtype, s);
+        return launch_out<false, false, false>(g, c_dtype, s);
+    }
+    if (kind == 1) return launch_out<true, false, false>(g, c_dtype, s);
+    // NVFP4: re-express both operands, then the FP8 product with the tensor scales
+    const int64_t ga = g.M * (g.K / 32), gb = g.N * (g.K / 32);
+    hipLaunchKernelGGL(k_nv_to_fp8, dim3((unsigned)((ga + 255) / 256)), dim3(256), 0, s, g.a, g.sa, g.M, g.K, g.a8, g.sa8);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_nv_to_fp8, dim3((unsigned)((gb + 255) / 256)), dim3(256), 0, s, g.b, g.sb, g.N, g.K, g.b8, g.sb8);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    GemmArgs h = g;
+    h.a = g.a8;
+    h.b = g.b8;
+    h.sa = g.sa8;
+    h.sb = g.sb8;
+    return launch_out<true, false, true>(h, c_dtype, s);
+}
+
+}  // namespace bgf

@@ -1,0 +1,758 @@
+// Fused rotate + quantize, dequantize and the rotation alone, for gfx950.
+//
+// Work unit: one lane owns one "segment", 32 consecutive elements of a row (64 B of bf16 or 128 B
+// of fp32, loaded with 128-bit loads). A 32-element MX group is then exactly one lane, a
+// 16-element NVFP4 block half a lane, and a Hadamard chunk of n elements n/32 adjacent lanes:
+//  - n <= 32: all butterfly stages run inside the lane's registers;
+//  - n = 64, 128, 256: stages h = 1..16 run in registers, then h = 32, 64, 128 pair lane l with
+//    lane l ^ 1, ^ 2, ^ 4 through DPP (quad permutes; ^4 as half-row mirror + quad reverse).
+// Each stage computes partner + (+-1) * self in one fused multiply-add, which equals the
+// butterfly's sum / difference exactly, in the same stage order as the definition (h ascending,
+// then one multiply by RN(1/sqrt(n))), so rotated values are bit-identical to that order.
+// Group amax, scale encode, element rounding (hardware RNE convert, or Philox-driven stochastic
+// rounding in software) and nibble packing then happen in registers; each lane stores 16 B of
+// codes (32 B for E4M3) and its block scale(s).
+//
+// 2D (32 x 32) blocks: a workgroup covers 32 rows x 8 segments; the tile max goes through LDS.
+// Per-row / per-tensor blocks (any even width, no rotation) use a row-per-workgroup kernel.
+#include <float.h>
+
+#include "device.h"
+#include "fp4_internal.h"
+
+namespace bgf {
+
+constexpr int kThreads = 256;
+
+template <int IN>
+__device__ __forceinline__ void load_segment(const void* base, float (&v)[32]) {
+    if constexpr (IN == DT_BF16) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(base);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 w = __builtin_nontemporal_load(p + i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[8 * i + 2 * j] = bf16_lo(w[j]);
+                v[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+            }
+        }
+    } else {
+        const f32x4* p = reinterpret_cast<const f32x4*>(base);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const f32x4 w = __builtin_nontemporal_load(p + i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[4 * i + j] = w[j];
+        }
+    }
+}
+
+// Blockwise H_n / sqrt(n) on the segment (see the file comment for the lane mapping).
+template <int HN>
+__device__ __forceinline__ void fwht_segment(float (&v)[32]) {
+    if constexpr (HN > 0) {
+        constexpr int HIN = HN < 32 ? HN : 32;  // in-register extent
+#pragma unroll
+        for (int h = 1; h < HIN; h <<= 1) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                if (!(i & h)) {
+                    const float a = v[i], b = v[i + h];
+                    v[i] = a + b;
+                    v[i + h] = a - b;
+                }
+            }
+        }
+        if constexpr (HN >= 64) {
+            const int lane = __lane_id();
+#pragma unroll
+            for (int m = 1; m < HN / 32; m <<= 1) {
+                const float sgn = (lane & m) ? -1.0f : 1.0f;
+#pragma unroll
+                for (int i = 0; i < 32; ++i) {
+                    float partner;
+                    if (m == 1) partner = lane_xor<1>(v[i]);
+                    else if (m == 2) partner = lane_xor<2>(v[i]);
+                    else partner = lane_xor<4>(v[i]);
+                    // lower lane: partner + self = a + b; upper lane: partner - self = a - b
+                    v[i] = __builtin_fmaf(v[i], sgn, partner);
+                }
+            }
+        }
+        const float c = inv_sqrt_n<HN>();
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = v[i] * c;
+    }
+}
+
+template <int B, int OFF>
+__device__ __forceinline__ float block_amax(const float (&v)[32]) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = OFF; i < OFF + B; ++i) m = fmaxf(m, fabsf(v[i]));
+    return m;
+}
+
+// Philox words for elements idx0 .. idx0 + 31 (idx0 a multiple of 32): u16 for element j is the
+// low (even j) / high (odd j) half of word (j >> 1) & 3 of the call for counter (idx0 + j) >> 3.
+__device__ __forceinline__ void philox_segment(uint64_t seed, uint64_t idx0, uint32_t (&w)[16]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint64_t ctr = (idx0 >> 3) + (uint64_t)g;
+        uint32_t c0 = (uint32_t)ctr, c1 = (uint32_t)(ctr >> 32), c2 = 0u, c3 = 0u;
+        philox4x32_10(c0, c1, c2, c3, (uint32_t)seed, (uint32_t)(seed >> 32));
+        w[4 * g + 0] = c0;
+        w[4 * g + 1] = c1;
+        w[4 * g + 2] = c2;
+        w[4 * g + 3] = c3;
+    }
+}
+__device__ __forceinline__ uint32_t sr_u16(const uint32_t (&w)[16], int j) {
+    const uint32_t word = w[j >> 1];
+    return (j & 1) ? (word >> 16) : (word & 0xFFFFu);
+}
+
+// Encode elements [OFF, OFF + B) of v into out (nibbles for E2M1: element j -> nibble j of the
+// 16-byte segment; bytes for E4M3). Scale arguments:
+//  pow2: the block scale is 2^k (k >= -126 after the caller's adjustment): the hardware convert
+//        divides by it exactly (RNE); SR multiplies by rcp = 2^-k exactly.
+//  else: elements are v * rcp (RN), converted with scale 1.
+template <int ELEM, int RND, int B, int OFF>
+__device__ __forceinline__ void encode_block(float (&v)[32], bool pow2, float cvt_scale, float rcp,
+                                             float clampv, const uint32_t (&rw)[16],
+                                             uint32_t (&out)[8]) {
+    if constexpr (RND == RND_RNE) {
+        if (!pow2) {
+#pragma unroll
+            for (int i = OFF; i < OFF + B; ++i) v[i] = v[i] * rcp;
+        }
+        if constexpr (ELEM == ELEM_E2M1) {
+#pragma unroll
+            for (int w = OFF / 8; w < (OFF + B) / 8; ++w) {
+                uint32_t r = 0u;
+                r = cvt_fp4x2<0>(r, v[8 * w + 0], v[8 * w + 1], cvt_scale);
+                r = cvt_fp4x2<1>(r, v[8 * w + 2], v[8 * w + 3], cvt_scale);
+                r = cvt_fp4x2<2>(r, v[8 * w + 4], v[8 * w + 5], cvt_scale);
+                r = cvt_fp4x2<3>(r, v[8 * w + 6], v[8 * w + 7], cvt_scale);
+                out[w] = r;
+            }
+        } else {
+#pragma unroll
+            for (int w = OFF / 4; w < (OFF + B) / 4; ++w) {
+                // saturate at +-448 (times the scale) before the non-saturating convert
+                const float a0 = __builtin_amdgcn_fmed3f(v[4 * w + 0], -clampv, clampv);
+                const float a1 = __builtin_amdgcn_fmed3f(v[4 * w + 1], -clampv, clampv);
+                const float a2 = __builtin_amdgcn_fmed3f(v[4 * w + 2], -clampv, clampv);
+                const float a3 = __builtin_amdgcn_fmed3f(v[4 * w + 3], -clampv, clampv);
+                uint32_t r = 0u;
+                r = cvt_fp8x2<false>(r, a0, a1, cvt_scale);
+                r = cvt_fp8x2<true>(r, a2, a3, cvt_scale);
+                out[w] = r;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = OFF; i < OFF + B; ++i) v[i] = v[i] * rcp;
+        if constexpr (ELEM == ELEM_E2M1) {
+#pragma unroll
+            for (int w = OFF / 8; w < (OFF + B) / 8; ++w) {
+                uint32_t r = 0u;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) r |= e2m1_sr(v[8 * w + j], sr_u16(rw, 8 * w + j)) << (4 * j);
+                out[w] = r;
+            }
+        } else {
+#pragma unroll
+            for (int w = OFF / 4; w < (OFF + B) / 4; ++w) {
+                uint32_t r = 0u;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) r |= e4m3_sr(v[4 * w + j], sr_u16(rw, 4 * w + j)) << (8 * j);
+                out[w] = r;
+            }
+        }
+    }
+}
+
+// E8M0 path for one block: returns the scale byte; encodes into out.
+template <int ELEM, int RND, int B, int OFF>
+__device__ __forceinline__ uint32_t e8m0_block(float (&v)[32], float amax, bool ceil_rule,
+                                               const uint32_t (&rw)[16], uint32_t (&out)[8]) {
+    int k = (ELEM == ELEM_E2M1) ? e8m0_exp<2, 0x400000u>(amax, ceil_rule)
+                                : e8m0_exp<8, 0x600000u>(amax, ceil_rule);
+    const uint32_t sbyte = (uint32_t)(k + 127);
+    if (k == -127) {
+        // 2^-127 is not a normal fp32: divide by 2^-126 after doubling (exact for such tiny x)
+#pragma unroll
+        for (int i = OFF; i < OFF + B; ++i) v[i] = v[i] * 2.0f;
+        k = -126;
+    }
+    const float scale = pow2f(k);
+    const float rcp = __builtin_amdgcn_ldexpf(1.0f, -k);
+    const float clampv = 448.0f * scale;
+    encode_block<ELEM, RND, B, OFF>(v, true, scale, rcp, clampv, rw, out);
+    return sbyte;
+}
+
+// NVFP4 candidate: s = E4M3(amax_b / RN(M g)), d = RN(val(s) g)
+__device__ __forceinline__ uint32_t nv_candidate(float amax, float g, float M, float& d) {
+    const float t = amax / (M * g);
+    const uint32_t s = e4m3_code_sat(t);
+    d = e4m3_value(s) * g;
+    return s;
+}
+
+// block SSE of RNE encoding with scale d (fixed pairwise tree over the 16 terms)
+template <int OFF>
+__device__ __forceinline__ float sse16(const float (&v)[32], float d) {
+    const float r = scale_recip(d);
+    float t[16];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+        const float a = v[OFF + i] * r, b = v[OFF + i + 1] * r;
+        const uint32_t q = cvt_fp4x2<0>(0u, a, b, 1.0f);
+        const v2f dq = fp4x2_to_f32<0>(q);
+        const float e0 = v[OFF + i] - dq[0] * d;
+        const float e1 = v[OFF + i + 1] - dq[1] * d;
+        t[i] = e0 * e0;
+        t[i + 1] = e1 * e1;
+    }
+#pragma unroll
+    for (int w = 16; w > 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w / 2; ++i) t[i] = t[2 * i] + t[2 * i + 1];
+    return t[0];
+}
+
+// NVFP4 path for one 16-element block: returns the E4M3 scale code.
+template <int RND, int OFF>
+__device__ __forceinline__ uint32_t nv_block(float (&v)[32], float amax, float g, bool four_six,
+                                             const uint32_t (&rw)[16], uint32_t (&out)[8]) {
+    float d;
+    uint32_t s = nv_candidate(amax, g, 6.0f, d);
+    if (four_six) {
+        float d4;
+        const uint32_t s4 = nv_candidate(amax, g, 4.0f, d4);
+        const float e6 = sse16<OFF>(v, d), e4 = sse16<OFF>(v, d4);
+        if (e4 < e6) {
+            s = s4;
+            d = d4;
+        }
+    }
+    encode_block<ELEM_E2M1, RND, 16, OFF>(v, false, 1.0f, scale_recip(d), 448.0f, rw, out);
+    return s;
+}
+
+// fp32-scale path for one block: writes the scale value.
+template <int ELEM, int RND, int B, int OFF>
+__device__ __forceinline__ float f32_block(float (&v)[32], float amax, const uint32_t (&rw)[16],
+                                           uint32_t (&out)[8]) {
+    const float d = amax / (ELEM == ELEM_E2M1 ? 6.0f : 448.0f);
+    encode_block<ELEM, RND, B, OFF>(v, false, 1.0f, scale_recip(d), 448.0f, rw, out);
+    return d;
+}
+
+// ---------------------------------------------------------------------------------------------
+// The segment kernel (1D groups, 2D tiles, amax pass, rotation pass)
+// ---------------------------------------------------------------------------------------------
+template <int IN, int HN, int ELEM, int SC, int RND, int BR, int BC, int PASS>
+__global__ __launch_bounds__(kThreads) void k_segment(SegArgs a) {
+    const int64_t spr = a.cols >> 5;  // segments per row
+    int64_t row, sc;
+    bool valid;
+    if constexpr (BR == 1) {
+        const int64_t seg = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+        valid = seg < a.nseg;
+        row = valid ? seg / spr : 0;
+        sc = valid ? seg - row * spr : 0;
+    } else {
+        const int64_t ngc = (spr + 7) >> 3;
+        const int64_t R = blockIdx.x / ngc, C = blockIdx.x - (blockIdx.x / ngc) * ngc;
+        row = R * 32 + (threadIdx.x >> 3);
+        sc = C * 8 + (threadIdx.x & 7);
+        valid = sc < spr;
+    }
+    const int64_t seg = row * spr + sc;
+    const int64_t c0 = sc * 32;
+
+    float v[32];
+    if (valid) {
+        const char* base = reinterpret_cast<const char*>(a.x) +
+                           (row * a.ldx + c0) * (IN == DT_BF16 ? 2 : 4);
+        load_segment<IN>(base, v);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+    }
+    fwht_segment<HN>(v);
+
+    if constexpr (PASS == PASS_ROTATE) {
+        if (valid) {
+            float4* y = reinterpret_cast<float4*>(a.yrot + row * a.cols + c0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) y[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+        }
+        return;
+    }
+    if constexpr (PASS == PASS_AMAX) {
+        float m = block_amax<32, 0>(v);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if (__lane_id() == 0) atomicMax(a.ws, __float_as_uint(m));
+        return;
+    }
+    if constexpr (PASS == PASS_QUANT) {
+        uint32_t rw[16];
+        if constexpr (RND == RND_SR) {
+            philox_segment(a.seed, (uint64_t)(row * a.cols + c0), rw);
+        }
+        uint32_t out[8];
+        if constexpr (BR == 32) {
+            // tile max over 32 rows: thread (r, j) of the 32 x 8 layout
+            __shared__ float tile[kThreads];
+            tile[threadIdx.x] = block_amax<32, 0>(v);
+            __syncthreads();
+            float m = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) m = fmaxf(m, tile[r * 8 + (threadIdx.x & 7)]);
+            const uint32_t s = e8m0_block<ELEM, RND, 32, 0>(v, m, a.ceil_rule != 0, rw, out);
+            if (valid && (threadIdx.x >> 3) == 0)
+                reinterpret_cast<uint8_t*>(a.scales)[(row >> 5) * spr + sc] = (uint8_t)s;
+        } else if constexpr (SC == SC_E8M0) {
+            if constexpr (BC == 32) {
+                const uint32_t s = e8m0_block<ELEM, RND, 32, 0>(v, block_amax<32, 0>(v), a.ceil_rule != 0, rw, out);
+                if (valid) reinterpret_cast<uint8_t*>(a.scales)[seg] = (uint8_t)s;
+            } else {
+                const float m0 = block_amax<16, 0>(v), m1 = block_amax<16, 16>(v);
+                const uint32_t s0 = e8m0_block<ELEM, RND, 16, 0>(v, m0, a.ceil_rule != 0, rw, out);
+                const uint32_t s1 = e8m0_block<ELEM, RND, 16, 16>(v, m1, a.ceil_rule != 0, rw, out);
+                if (valid) reinterpret_cast<uint16_t*>(a.scales)[seg] = (uint16_t)(s0 | (s1 << 8));
+            }
+        } else if constexpr (SC == SC_NV) {
+            const float amax_t = __uint_as_float(*a.ws);
+            const float g = amax_t > 0.0f ? amax_t / 2688.0f : 1.0f;
+            if (blockIdx.x == 0 && threadIdx.x == 0) *a.tensor_scale = g;
+            const float m0 = block_amax<16, 0>(v), m1 = block_amax<16, 16>(v);
+            const uint32_t s0 = nv_block<RND, 0>(v, m0, g, a.four_six != 0, rw, out);
+            const uint32_t s1 = nv_block<RND, 16>(v, m1, g, a.four_six != 0, rw, out);
+            if (valid) reinterpret_cast<uint16_t*>(a.scales)[seg] = (uint16_t)(s0 | (s1 << 8));
+        } else {  // SC_F32
+            if constexpr (BC == 32) {
+                const float d = f32_block<ELEM, RND, 32, 0>(v, block_amax<32, 0>(v), rw, out);
+                if (valid) reinterpret_cast<float*>(a.scales)[seg] = d;
+            } else {
+                const float m0 = block_amax<16, 0>(v), m1 = block_amax<16, 16>(v);
+                const float d0 = f32_block<ELEM, RND, 16, 0>(v, m0, rw, out);
+                const float d1 = f32_block<ELEM, RND, 16, 16>(v, m1, rw, out);
+                if (valid) reinterpret_cast<float2*>(a.scales)[seg] = make_float2(d0, d1);
+            }
+        }
+        if (valid) {
+            if constexpr (ELEM == ELEM_E2M1) {
+                uint4* dst = reinterpret_cast<uint4*>(a.codes + seg * 16);
+                *dst = make_uint4(out[0], out[1], out[2], out[3]);
+            } else {
+                uint4* dst = reinterpret_cast<uint4*>(a.codes + seg * 32);
+                dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+                dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Per-row / per-tensor blocks: one workgroup per row, any even width, no rotation
+// ---------------------------------------------------------------------------------------------
+template <int IN>
+__device__ __forceinline__ float load_elem(const void* x, int64_t i) {
+    if constexpr (IN == DT_BF16) return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(x)[i] << 16);
+    return reinterpret_cast<const float*>(x)[i];
+}
+
+template <int IN>
+__global__ __launch_bounds__(kThreads) void k_amax_rows(const void* x, int64_t rows, int64_t cols,
+                                                        int64_t ldx, uint32_t* ws) {
+    __shared__ float red[kThreads];
+    float m = 0.0f;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x)
+        for (int64_t c = threadIdx.x; c < cols; c += kThreads) m = fmaxf(m, fabsf(load_elem<IN>(x, r * ldx + c)));
+    red[threadIdx.x] = m;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+        if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) atomicMax(ws, __float_as_uint(red[0]));
+}
+
+template <int IN, int ELEM, int SC, int RND>
+__global__ __launch_bounds__(kThreads) void k_rowblock(RowArgs a) {
+    __shared__ float red[kThreads];
+    const int64_t row = blockIdx.x;
+    const void* xr = reinterpret_cast<const char*>(a.x) + row * a.ldx * (IN == DT_BF16 ? 2 : 4);
+    float amax;
+    if (a.per_tensor) {
+        amax = __uint_as_float(*a.ws);
+    } else {
+        float m = 0.0f;
+        for (int64_t c = threadIdx.x; c < a.cols; c += kThreads) m = fmaxf(m, fabsf(load_elem<IN>(xr, c)));
+        red[threadIdx.x] = m;
+        __syncthreads();
+        for (int s = kThreads / 2; s > 0; s >>= 1) {
+            if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+            __syncthreads();
+        }
+        amax = red[0];
+    }
+    // scale
+    float rcp, cvt_scale = 1.0f, clampv = 448.0f;
+    bool pow2 = false;
+    float pre = 1.0f;
+    const int64_t sidx = a.per_tensor ? 0 : row;
+    const bool writer = threadIdx.x == 0 && (!a.per_tensor || row == 0);
+    if constexpr (SC == SC_E8M0) {
+        int k = (ELEM == ELEM_E2M1) ? e8m0_exp<2, 0x400000u>(amax, a.ceil_rule != 0)
+                                    : e8m0_exp<8, 0x600000u>(amax, a.ceil_rule != 0);
+        if (writer) reinterpret_cast<uint8_t*>(a.scales)[sidx] = (uint8_t)(k + 127);
+        if (k == -127) {
+            pre = 2.0f;
+            k = -126;
+        }
+        pow2 = true;
+        cvt_scale = pow2f(k);
+        rcp = __builtin_amdgcn_ldexpf(1.0f, -k);
+        clampv = 448.0f * cvt_scale;
+    } else {
+        const float d = amax / (ELEM == ELEM_E2M1 ? 6.0f : 448.0f);
+        if (writer) reinterpret_cast<float*>(a.scales)[sidx] = d;
+        rcp = scale_recip(d);
+    }
+    // elements, two per step
+    for (int64_t p = threadIdx.x; p < a.cols / 2; p += kThreads) {
+        float x0 = load_elem<IN>(xr, 2 * p) * pre, x1 = load_elem<IN>(xr, 2 * p + 1) * pre;
+        const uint64_t idx = (uint64_t)(row * a.cols + 2 * p);
+        uint32_t q0, q1;
+        if constexpr (RND == RND_SR) {
+            x0 = x0 * rcp;
+            x1 = x1 * rcp;
+            uint32_t c0 = (uint32_t)(idx >> 3), c1 = (uint32_t)(idx >> 35), c2 = 0u, c3 = 0u;
+            philox4x32_10(c0, c1, c2, c3, (uint32_t)a.seed, (uint32_t)(a.seed >> 32));
+            const uint32_t words[4] = {c0, c1, c2, c3};
+            const uint32_t w = words[(idx >> 1) & 3];  // idx even: this word holds both uniforms
+            if constexpr (ELEM == ELEM_E2M1) {
+                q0 = e2m1_sr(x0, w & 0xFFFFu);
+                q1 = e2m1_sr(x1, w >> 16);
+            } else {
+                q0 = e4m3_sr(x0, w & 0xFFFFu);
+                q1 = e4m3_sr(x1, w >> 16);
+            }
+        } else {
+            if (!pow2) {
+                x0 = x0 * rcp;
+                x1 = x1 * rcp;
+            }
+            if constexpr (ELEM == ELEM_E2M1) {
+                const uint32_t r = cvt_fp4x2<0>(0u, x0, x1, cvt_scale);
+                q0 = r & 0xFu;
+                q1 = (r >> 4) & 0xFu;
+            } else {
+                const uint32_t r = cvt_fp8x2<false>(0u, __builtin_amdgcn_fmed3f(x0, -clampv, clampv),
+                                                    __builtin_amdgcn_fmed3f(x1, -clampv, clampv), cvt_scale);
+                q0 = r & 0xFFu;
+                q1 = (r >> 8) & 0xFFu;
+            }
+        }
+        if constexpr (ELEM == ELEM_E2M1) {
+            a.codes[row * (a.cols / 2) + p] = (uint8_t)(q0 | (q1 << 4));
+        } else {
+            a.codes[row * a.cols + 2 * p] = (uint8_t)q0;
+            a.codes[row * a.cols + 2 * p + 1] = (uint8_t)q1;
+        }
+    }
+}
+
+__global__ void k_zero_u32(uint32_t* p, int n) {
+    if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Dequantize
+// ---------------------------------------------------------------------------------------------
+template <int ELEM, int SC, int HN, int BR, int BC, int OUT>
+__global__ __launch_bounds__(kThreads) void k_dequant_segment(DeqArgs a) {
+    const int64_t seg = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const bool valid = seg < a.nseg;
+    const int64_t spr = a.cols >> 5;
+    const int64_t row = valid ? seg / spr : 0;
+    const int64_t sc = valid ? seg - row * spr : 0;
+    float v[32];
+    if (valid) {
+        // block scales of this segment
+        float d0, d1;
+        if constexpr (SC == SC_F32) {
+            const float* s = reinterpret_cast<const float*>(a.scales);
+            if constexpr (BC == 32) d0 = d1 = s[(row / BR) * spr + sc];
+            else { d0 = s[2 * seg]; d1 = s[2 * seg + 1]; }
+        } else {
+            const uint8_t* s = reinterpret_cast<const uint8_t*>(a.scales);
+            uint32_t b0, b1;
+            if constexpr (BC == 32) b0 = b1 = s[(row / BR) * spr + sc];
+            else { b0 = s[2 * seg]; b1 = s[2 * seg + 1]; }
+            if constexpr (SC == SC_E8M0) {
+                d0 = __builtin_amdgcn_ldexpf(1.0f, (int)b0 - 127);
+                d1 = __builtin_amdgcn_ldexpf(1.0f, (int)b1 - 127);
+            } else {
+                const float g = *a.tensor_scale;
+                d0 = e4m3_value(b0 & 0x7Fu) * g;
+                d1 = e4m3_value(b1 & 0x7Fu) * g;
+            }
+        }
+        if constexpr (ELEM == ELEM_E2M1) {
+            const uint4 q = *reinterpret_cast<const uint4*>(a.codes + seg * 16);
+            const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const v2f p0 = fp4x2_to_f32<0>(qw[w]), p1 = fp4x2_to_f32<1>(qw[w]);
+                const v2f p2 = fp4x2_to_f32<2>(qw[w]), p3 = fp4x2_to_f32<3>(qw[w]);
+                const float d = (w < 2) ? d0 : d1;
+                v[8 * w + 0] = p0[0] * d;
+                v[8 * w + 1] = p0[1] * d;
+                v[8 * w + 2] = p1[0] * d;
+                v[8 * w + 3] = p1[1] * d;
+                v[8 * w + 4] = p2[0] * d;
+                v[8 * w + 5] = p2[1] * d;
+                v[8 * w + 6] = p3[0] * d;
+                v[8 * w + 7] = p3[1] * d;
+            }
+        } else {
+            const uint4* src = reinterpret_cast<const uint4*>(a.codes + seg * 32);
+            const uint4 q0 = src[0], q1 = src[1];
+            const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const v2f p0 = fp8x2_to_f32<false>(qw[w]), p1 = fp8x2_to_f32<true>(qw[w]);
+                const float d = (w < 4) ? d0 : d1;
+                v[4 * w + 0] = p0[0] * d;
+                v[4 * w + 1] = p0[1] * d;
+                v[4 * w + 2] = p1[0] * d;
+                v[4 * w + 3] = p1[1] * d;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+    }
+    fwht_segment<HN>(v);
+    if (!valid) return;
+    char* base = reinterpret_cast<char*>(a.y) + (row * a.ldy + sc * 32) * (OUT == DT_BF16 ? 2 : 4);
+    if constexpr (OUT == DT_F32) {
+        float4* y = reinterpret_cast<float4*>(base);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    } else {
+        uint4* y = reinterpret_cast<uint4*>(base);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t w[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                w[j] = bf16_rne_bits(v[8 * i + 2 * j]) | (bf16_rne_bits(v[8 * i + 2 * j + 1]) << 16);
+            y[i] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+}
+
+// per-row / per-tensor layouts (any even width): element-wise
+template <int ELEM, int SC, int OUT>
+__global__ __launch_bounds__(kThreads) void k_dequant_rowblock(DeqArgs a) {
+    const int64_t row = blockIdx.x;
+    const int64_t sidx = a.per_tensor ? 0 : row;
+    float d;
+    if constexpr (SC == SC_F32) d = reinterpret_cast<const float*>(a.scales)[sidx];
+    else d = __builtin_amdgcn_ldexpf(1.0f, (int)reinterpret_cast<const uint8_t*>(a.scales)[sidx] - 127);
+    for (int64_t c = threadIdx.x; c < a.cols; c += kThreads) {
+        float q;
+        if constexpr (ELEM == ELEM_E2M1) {
+            const uint32_t b = a.codes[row * (a.cols / 2) + c / 2];
+            const uint32_t nib = (c & 1) ? (b >> 4) : (b & 0xFu);
+            q = fp4x2_to_f32<0>(nib)[0];
+        } else {
+            q = fp8x2_to_f32<false>((uint32_t)a.codes[row * a.cols + c])[0];
+        }
+        const float y = q * d;
+        if constexpr (OUT == DT_F32) reinterpret_cast<float*>(a.y)[row * a.ldy + c] = y;
+        else reinterpret_cast<uint16_t*>(a.y)[row * a.ldy + c] = (uint16_t)bf16_rne_bits(y);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Host-side launchers (dispatch over the compile-time variants)
+// ---------------------------------------------------------------------------------------------
+#define BGF_LAUNCH(kern, grid, ...)                                                        \
+    do {                                                                                   \
+        hipLaunchKernelGGL((kern), dim3(grid), dim3(kThreads), 0, stream, __VA_ARGS__);    \
+        return hipGetLastError();                                                          \
+    } while (0)
+
+template <int IN, int HN, int ELEM, int SC, int RND, int BR, int BC>
+static hipError_t launch_seg_q(const SegArgs& a, int pass, hipStream_t stream) {
+    int64_t grid;
+    if (BR == 1) grid = (a.nseg + kThreads - 1) / kThreads;
+    else grid = (a.rows / 32) * (((a.cols >> 5) + 7) >> 3);
+    if (pass == PASS_AMAX) BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, 32, PASS_AMAX>), grid, a);
+    if (pass == PASS_ROTATE) BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, 32, PASS_ROTATE>), grid, a);
+    BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, BR, BC, PASS_QUANT>), grid, a);
+}
+
+template <int IN, int HN>
+static hipError_t dispatch_seg_hn(const SegArgs& a, int elem, int sc, int rnd, int br, int bc,
+                                  int pass, hipStream_t s) {
+    if (pass != PASS_QUANT) return launch_seg_q<IN, HN, ELEM_E2M1, SC_E8M0, RND_RNE, 1, 32>(a, pass, s);
+#define BGF_RB(E, S, R)                                                                    \
+    do {                                                                                   \
+        if (br == 32) return launch_seg_q<IN, HN, E, S, R, 32, 32>(a, pass, s);            \
+        if (bc == 32) return launch_seg_q<IN, HN, E, S, R, 1, 32>(a, pass, s);             \
+        return launch_seg_q<IN, HN, E, S, R, 1, 16>(a, pass, s);                           \
+    } while (0)
+    if (sc == SC_NV) {
+        if (rnd == RND_SR) return launch_seg_q<IN, HN, ELEM_E2M1, SC_NV, RND_SR, 1, 16>(a, pass, s);
+        return launch_seg_q<IN, HN, ELEM_E2M1, SC_NV, RND_RNE, 1, 16>(a, pass, s);
+    }
+    if (elem == ELEM_E2M1) {
+        if (sc == SC_E8M0) {
+            if (rnd == RND_SR) BGF_RB(ELEM_E2M1, SC_E8M0, RND_SR);
+            BGF_RB(ELEM_E2M1, SC_E8M0, RND_RNE);
+        }
+        if (rnd == RND_SR) {
+            if (bc == 32) return launch_seg_q<IN, HN, ELEM_E2M1, SC_F32, RND_SR, 1, 32>(a, pass, s);
+            return launch_seg_q<IN, HN, ELEM_E2M1, SC_F32, RND_SR, 1, 16>(a, pass, s);
+        }
+        if (bc == 32) return launch_seg_q<IN, HN, ELEM_E2M1, SC_F32, RND_RNE, 1, 32>(a, pass, s);
+        return launch_seg_q<IN, HN, ELEM_E2M1, SC_F32, RND_RNE, 1, 16>(a, pass, s);
+    }
+    // E4M3 elements: E8M0 or fp32 scales
+    if (sc == SC_F32) {
+        if (rnd == RND_SR) {
+            if (bc == 32) return launch_seg_q<IN, HN, ELEM_E4M3, SC_F32, RND_SR, 1, 32>(a, pass, s);
+            return launch_seg_q<IN, HN, ELEM_E4M3, SC_F32, RND_SR, 1, 16>(a, pass, s);
+        }
+        if (bc == 32) return launch_seg_q<IN, HN, ELEM_E4M3, SC_F32, RND_RNE, 1, 32>(a, pass, s);
+        return launch_seg_q<IN, HN, ELEM_E4M3, SC_F32, RND_RNE, 1, 16>(a, pass, s);
+    }
+    if (rnd == RND_SR) BGF_RB(ELEM_E4M3, SC_E8M0, RND_SR);
+    BGF_RB(ELEM_E4M3, SC_E8M0, RND_RNE);
+#undef BGF_RB
+}
+
+hipError_t launch_segment(const SegArgs& a, int in_dtype, int hn, int elem, int sc, int rnd, int br,
+                          int bc, int pass, hipStream_t s) {
+#define BGF_HN(IN)                                                                         \
+    switch (hn) {                                                                          \
+        case 0: return dispatch_seg_hn<IN, 0>(a, elem, sc, rnd, br, bc, pass, s);          \
+        case 16: return dispatch_seg_hn<IN, 16>(a, elem, sc, rnd, br, bc, pass, s);        \
+        case 32: return dispatch_seg_hn<IN, 32>(a, elem, sc, rnd, br, bc, pass, s);        \
+        case 64: return dispatch_seg_hn<IN, 64>(a, elem, sc, rnd, br, bc, pass, s);        \
+        case 128: return dispatch_seg_hn<IN, 128>(a, elem, sc, rnd, br, bc, pass, s);      \
+        case 256: return dispatch_seg_hn<IN, 256>(a, elem, sc, rnd, br, bc, pass, s);      \
+        default: return hipErrorInvalidValue;                                              \
+    }
+    if (in_dtype == DT_BF16) { BGF_HN(DT_BF16) }
+    BGF_HN(DT_F32)
+#undef BGF_HN
+}
+
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream) {
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, stream, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_amax_rows(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                            uint32_t* ws, hipStream_t stream) {
+    const int64_t grid = rows < 4096 ? rows : 4096;
+    if (in_dtype == DT_BF16) BGF_LAUNCH(k_amax_rows<DT_BF16>, grid, x, rows, cols, ldx, ws);
+    BGF_LAUNCH(k_amax_rows<DT_F32>, grid, x, rows, cols, ldx, ws);
+}
+
+hipError_t launch_rowblock(const RowArgs& a, int in_dtype, int elem, int sc, int rnd,
+                           hipStream_t stream) {
+#define BGF_RBK(IN)                                                                        \
+    do {                                                                                   \
+        if (elem == ELEM_E2M1) {                                                           \
+            if (sc == SC_E8M0) {                                                           \
+                if (rnd == RND_SR) BGF_LAUNCH((k_rowblock<IN, ELEM_E2M1, SC_E8M0, RND_SR>), a.rows, a); \
+                BGF_LAUNCH((k_rowblock<IN, ELEM_E2M1, SC_E8M0, RND_RNE>), a.rows, a);     \
+            }                                                                              \
+            if (rnd == RND_SR) BGF_LAUNCH((k_rowblock<IN, ELEM_E2M1, SC_F32, RND_SR>), a.rows, a); \
+            BGF_LAUNCH((k_rowblock<IN, ELEM_E2M1, SC_F32, RND_RNE>), a.rows, a);          \
+        }                                                                                  \
+        if (sc == SC_E8M0) {                                                               \
+            if (rnd == RND_SR) BGF_LAUNCH((k_rowblock<IN, ELEM_E4M3, SC_E8M0, RND_SR>), a.rows, a); \
+            BGF_LAUNCH((k_rowblock<IN, ELEM_E4M3, SC_E8M0, RND_RNE>), a.rows, a);         \
+        }                                                                                  \
+        if (rnd == RND_SR) BGF_LAUNCH((k_rowblock<IN, ELEM_E4M3, SC_F32, RND_SR>), a.rows, a); \
+        BGF_LAUNCH((k_rowblock<IN, ELEM_E4M3, SC_F32, RND_RNE>), a.rows, a);              \
+    } while (0)
+    if (in_dtype == DT_BF16) BGF_RBK(DT_BF16);
+    BGF_RBK(DT_F32);
+#undef BGF_RBK
+}
+
+template <int ELEM, int SC, int BR, int BC, int OUT>
+static hipError_t dq_hn(const DeqArgs& a, int hn, hipStream_t stream) {
+    const int64_t grid = (a.nseg + kThreads - 1) / kThreads;
+    switch (hn) {
+        case 0: BGF_LAUNCH((k_dequant_segment<ELEM, SC, 0, BR, BC, OUT>), grid, a);
+        case 16: BGF_LAUNCH((k_dequant_segment<ELEM, SC, 16, BR, BC, OUT>), grid, a);
+        case 32: BGF_LAUNCH((k_dequant_segment<ELEM, SC, 32, BR, BC, OUT>), grid, a);
+        case 64: BGF_LAUNCH((k_dequant_segment<ELEM, SC, 64, BR, BC, OUT>), grid, a);
+        case 128: BGF_LAUNCH((k_dequant_segment<ELEM, SC, 128, BR, BC, OUT>), grid, a);
+        case 256: BGF_LAUNCH((k_dequant_segment<ELEM, SC, 256, BR, BC, OUT>), grid, a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int OUT>
+static hipError_t dq_out(const DeqArgs& a, int elem, int sc, int br, int bc, int hn, hipStream_t s) {
+    if (sc == SC_NV) return dq_hn<ELEM_E2M1, SC_NV, 1, 16, OUT>(a, hn, s);
+    if (elem == ELEM_E2M1) {
+        if (sc == SC_F32) {
+            if (bc == 32) return dq_hn<ELEM_E2M1, SC_F32, 1, 32, OUT>(a, hn, s);
+            return dq_hn<ELEM_E2M1, SC_F32, 1, 16, OUT>(a, hn, s);
+        }
+        if (br == 32) return dq_hn<ELEM_E2M1, SC_E8M0, 32, 32, OUT>(a, hn, s);
+        if (bc == 32) return dq_hn<ELEM_E2M1, SC_E8M0, 1, 32, OUT>(a, hn, s);
+        return dq_hn<ELEM_E2M1, SC_E8M0, 1, 16, OUT>(a, hn, s);
+    }
+    if (sc == SC_F32) {
+        if (bc == 32) return dq_hn<ELEM_E4M3, SC_F32, 1, 32, OUT>(a, hn, s);
+        return dq_hn<ELEM_E4M3, SC_F32, 1, 16, OUT>(a, hn, s);
+    }
+    if (br == 32) return dq_hn<ELEM_E4M3, SC_E8M0, 32, 32, OUT>(a, hn, s);
+    if (bc == 32) return dq_hn<ELEM_E4M3, SC_E8M0, 1, 32, OUT>(a, hn, s);
+    return dq_hn<ELEM_E4M3, SC_E8M0, 1, 16, OUT>(a, hn, s);
+}
+
+hipError_t launch_dequant_segment(const DeqArgs& a, int elem, int sc, int br, int bc, int hn,
+                                  int out_dtype, hipStream_t s) {
+    if (out_dtype == DT_BF16) return dq_out<DT_BF16>(a, elem, sc, br, bc, hn, s);
+    return dq_out<DT_F32>(a, elem, sc, br, bc, hn, s);
+}
+
+hipError_t launch_dequant_rowblock(const DeqArgs& a, int elem, int sc, int out_dtype,
+                                   hipStream_t stream) {
+    const int64_t grid = a.rows;
+#define BGF_DQR(OUT)                                                                       \
+    do {                                                                                   \
+        if (elem == ELEM_E2M1) {                                                           \
+            if (sc == SC_F32) BGF_LAUNCH((k_dequant_rowblock<ELEM_E2M1, SC_F32, OUT>), grid, a); \
+            BGF_LAUNCH((k_dequant_rowblock<ELEM_E2M1, SC_E8M0, OUT>), grid, a);           \
+        }                                                                                  \
+        if (sc == SC_F32) BGF_LAUNCH((k_dequant_rowblock<ELEM_E4M3, SC_F32, OUT>), grid, a); \
+        BGF_LAUNCH((k_dequant_rowblock<ELEM_E4M3, SC_E8M0, OUT>), grid, a);               \
+    } while (0)
+    if (out_dtype == DT_BF16) BGF_DQR(DT_BF16);
+    BGF_DQR(DT_F32);
+#undef BGF_DQR
+}
+
+}  // namespace bgf

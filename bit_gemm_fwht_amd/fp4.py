@@ -1,0 +1,235 @@
+"""Python binding of libbgf.so (the C ABI in include/fp4.h).
+
+Argument marshalling only: every step of quantize / dequantize / rotate / GEMM runs in the HIP
+kernels behind the C ABI. torch supplies device memory and the current stream. If the library is
+missing this module raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, replace
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbgf.so")
+
+# enums of include/fp4.h
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_WORKSPACE, ERR_HIP, ERR_INTERNAL = range(7)
+DT_F32, DT_BF16 = 0, 1
+E2M1, E4M3 = 0, 1
+SCALE_E8M0_FLOOR, SCALE_E8M0_CEIL, SCALE_NV, SCALE_NV_4OVER6, SCALE_F32 = range(5)
+ROUND_RNE, ROUND_SR = 0, 1
+
+
+class Fp4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class QParams(ctypes.Structure):
+    _fields_ = [("elem", ctypes.c_int32), ("block_rows", ctypes.c_int32),
+                ("block_cols", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
+                ("round_mode", ctypes.c_int32), ("hadamard_n", ctypes.c_int32),
+                ("seed", ctypes.c_uint64)]
+
+
+class QTensorC(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("tensor_scale", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("p", QParams)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbgf.so. Raises if it has not been built: there is no other implementation."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                          "g.build()'` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    QP = ctypes.POINTER(QParams)
+    QT = ctypes.POINTER(QTensorC)
+    L.fp4_abi_version.restype = ctypes.c_int
+    L.fp4_status_string.argtypes = [ctypes.c_int]
+    L.fp4_status_string.restype = ctypes.c_char_p
+    for name in ("fp4_codes_bytes", "fp4_scales_bytes", "fp4_workspace_bytes"):
+        getattr(L, name).argtypes = [I64, I64, QP]
+        getattr(L, name).restype = I64
+    L.fp4_quantize.argtypes = [P, I32, I64, I64, I64, QP, P, P, P, P, I64, P]
+    L.fp4_quantize.restype = ctypes.c_int
+    L.fp4_dequantize.argtypes = [P, P, P, I64, I64, QP, P, I32, I64, P]
+    L.fp4_dequantize.restype = ctypes.c_int
+    L.fp4_hadamard.argtypes = [P, I32, I64, I64, I64, I32, P, P]
+    L.fp4_hadamard.restype = ctypes.c_int
+    L.fp4_gemm_workspace_bytes.argtypes = [QT, QT]
+    L.fp4_gemm_workspace_bytes.restype = I64
+    L.fp4_gemm.argtypes = [QT, QT, P, I32, I64, QP, QT, P, I64, P]
+    L.fp4_gemm.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().fp4_status_string(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        raise Fp4Error(status, what)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DT_F32
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+@dataclass(frozen=True)
+class Params:
+    elem: int = E2M1
+    block: tuple = (1, 32)
+    scale_mode: int = SCALE_E8M0_FLOOR
+    round_mode: int = ROUND_RNE
+    hadamard_n: int = 0
+    seed: int = 0
+
+    def c(self) -> QParams:
+        return QParams(self.elem, self.block[0], self.block[1], self.scale_mode, self.round_mode,
+                       self.hadamard_n, self.seed)
+
+
+MXFP4 = Params()
+
+
+@dataclass
+class QTensor:
+    """A quantized [rows, cols] tensor: codes, scales and (NVFP4) the fp32 tensor scale."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tensor_scale: torch.Tensor | None
+    rows: int
+    cols: int
+    params: Params
+
+    def c(self) -> QTensorC:
+        ts = self.tensor_scale.data_ptr() if self.tensor_scale is not None else None
+        return QTensorC(self.codes.data_ptr(), self.scales.data_ptr(), ts, self.rows, self.cols,
+                        self.params.c())
+
+
+def buffer_sizes(rows: int, cols: int, params: Params) -> tuple[int, int, int]:
+    p = params.c()
+    L = lib()
+    cb = L.fp4_codes_bytes(rows, cols, ctypes.byref(p))
+    sb = L.fp4_scales_bytes(rows, cols, ctypes.byref(p))
+    wb = L.fp4_workspace_bytes(rows, cols, ctypes.byref(p))
+    if cb < 0 or sb < 0 or wb < 0:
+        raise Fp4Error(ERR_INVALID_ARG, f"quantize params {params} for shape ({rows}, {cols})")
+    return cb, sb, wb
+
+
+def empty_qtensor(rows: int, cols: int, params: Params, device) -> QTensor:
+    cb, sb, _ = buffer_sizes(rows, cols, params)
+    codes = torch.empty(max(cb, 1), dtype=torch.uint8, device=device)
+    scales = torch.empty(max(sb, 1), dtype=torch.uint8, device=device)
+    nv = params.scale_mode in (SCALE_NV, SCALE_NV_4OVER6)
+    ts = torch.empty(1, dtype=torch.float32, device=device) if nv else None
+    return QTensor(codes, scales, ts, rows, cols, params)
+
+
+def quantize(x: torch.Tensor, params: Params = MXFP4, out: QTensor | None = None,
+             workspace: torch.Tensor | None = None) -> QTensor:
+    """Quantize a 2-D float32 / bfloat16 CUDA tensor along its last axis."""
+    if x.dim() != 2 or not x.is_cuda:
+        raise ValueError("x must be a 2-D CUDA tensor")
+    if x.stride(1) != 1:
+        raise ValueError("x must be contiguous along its last axis")
+    rows, cols = x.shape
+    q = out if out is not None else empty_qtensor(rows, cols, params, x.device)
+    _, _, wb = buffer_sizes(rows, cols, params)
+    if wb and workspace is None:
+        workspace = torch.empty(wb, dtype=torch.uint8, device=x.device)
+    p = params.c()
+    ts = q.tensor_scale.data_ptr() if q.tensor_scale is not None else None
+    st = lib().fp4_quantize(x.data_ptr(), _dtype_code(x), rows, cols, x.stride(0), ctypes.byref(p),
+                            q.codes.data_ptr(), q.scales.data_ptr(), ts,
+                            workspace.data_ptr() if workspace is not None else None,
+                            workspace.numel() if workspace is not None else 0,
+                            _stream_ptr(x.device))
+    _check(st, "fp4_quantize")
+    return q
+
+
+def dequantize(q: QTensor, dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    y = out if out is not None else torch.empty(q.rows, q.cols, dtype=dtype, device=q.codes.device)
+    p = q.params.c()
+    ts = q.tensor_scale.data_ptr() if q.tensor_scale is not None else None
+    st = lib().fp4_dequantize(q.codes.data_ptr(), q.scales.data_ptr(), ts, q.rows, q.cols,
+                              ctypes.byref(p), y.data_ptr(), _dtype_code(y), y.stride(0),
+                              _stream_ptr(y.device))
+    _check(st, "fp4_dequantize")
+    return y
+
+
+def hadamard(x: torch.Tensor, n: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Blockwise H_n / sqrt(n) along the last axis (fp32 result)."""
+    rows, cols = x.shape
+    y = out if out is not None else torch.empty(rows, cols, dtype=torch.float32, device=x.device)
+    st = lib().fp4_hadamard(x.data_ptr(), _dtype_code(x), rows, cols, x.stride(0), n, y.data_ptr(),
+                            _stream_ptr(x.device))
+    _check(st, "fp4_hadamard")
+    return y
+
+
+def gemm_workspace_bytes(a: QTensor, b: QTensor) -> int:
+    ac, bc = a.c(), b.c()
+    n = lib().fp4_gemm_workspace_bytes(ctypes.byref(ac), ctypes.byref(bc))
+    if n < 0:
+        raise Fp4Error(ERR_UNSUPPORTED, "fp4_gemm_workspace_bytes")
+    return n
+
+
+def gemm(a: QTensor, b: QTensor, out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+         workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """C [M, N] = A [M, K] * B [N, K]^T on quantized operands (fp32 accumulation)."""
+    dev = a.codes.device
+    c = out if out is not None else torch.empty(a.rows, b.rows, dtype=out_dtype, device=dev)
+    wb = gemm_workspace_bytes(a, b)
+    if wb and workspace is None:
+        workspace = torch.empty(wb, dtype=torch.uint8, device=dev)
+    ac, bc = a.c(), b.c()
+    st = lib().fp4_gemm(ctypes.byref(ac), ctypes.byref(bc), c.data_ptr(), _dtype_code(c),
+                        c.stride(0), None, None,
+                        workspace.data_ptr() if workspace is not None else None,
+                        workspace.numel() if workspace is not None else 0, _stream_ptr(dev))
+    _check(st, "fp4_gemm")
+    return c
+
+
+def upload_qtensor(codes, scales, tensor_scale, rows, cols, params: Params, device) -> QTensor:
+    """Wrap host arrays (numpy) of an already-quantized tensor as a device QTensor."""
+    import numpy as np
+    ct = torch.from_numpy(np.ascontiguousarray(codes).reshape(-1).view(np.uint8)).to(device)
+    st = torch.from_numpy(np.ascontiguousarray(scales).reshape(-1).view(np.uint8)).to(device)
+    ts = None
+    if tensor_scale is not None:
+        ts = torch.from_numpy(np.ascontiguousarray(tensor_scale, dtype=np.float32).reshape(1)).to(device)
+    return QTensor(ct, st, ts, rows, cols, params)
+
+
+def with_params(q: QTensor, **kw) -> QTensor:
+    return QTensor(q.codes, q.scales, q.tensor_scale, q.rows, q.cols, replace(q.params, **kw))

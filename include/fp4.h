@@ -1,0 +1,163 @@
+/*
+ * fp4.h - C ABI of the MI355X (gfx950) block-scaled FP4 / FP8 quantize + GEMM library
+ * (libbgf.so, built from bit_gemm_fwht_amd/csrc).
+ *
+ * What it computes (sources cited by page title and section):
+ *  - the blockwise Hadamard rotation y = x (H_n / sqrt(n)) of the lecture notes "Quartet — Native
+ *    4-bit training that actually trains" (section on Hadamard rotation) and of §7 of the
+ *    caveduck.io post "low-bit quantization" (rotation to spread outliers, O(n log n));
+ *  - block-scaled quantization to FP4 E2M1 (the 15-value grid of that post's section
+ *    "FP4라는 무리수") or FP8 E4M3, with one shared scale per block: per tensor (§1), per row or
+ *    per 32-element group / MXFP4 (§2), power-of-two E8M0 scales (§3), 32x32 transposition-
+ *    invariant 2D blocks with truncation-free scales and stochastic rounding ("Stable FP4 Training
+ *    via Transposition-Invariant Block Quantization", abstract), NVFP4 16-element blocks with an
+ *    E4M3 block scale and an fp32 tensor scale, and the adaptive 4/6 choice ("Four Over Six: More
+ *    Accurate NVFP4 Quantization with Adaptive Block Scaling", methodology);
+ *  - the GEMM on the quantized operands, one call, fp32 accumulation (the QuTLASS kernel list
+ *    of the Quartet notes: 4-bit GEMM, online quantization of the output).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named x, y, codes, scales, tensor_scale, C and workspace are DEVICE pointers
+ *    (memory of the current HIP device); fp4_qparams / fp4_qtensor structs are HOST pointers.
+ *  - The caller owns every buffer and keeps it alive until the work queued on `stream` (a
+ *    hipStream_t, or NULL for the default stream) has completed. The library allocates nothing,
+ *    keeps no pointer after returning and holds no mutable global state: calls on different
+ *    streams may run concurrently.
+ *  - All work is queued asynchronously on `stream`; a return of FP4_OK means "queued".
+ *  - Every argument is validated on the host before anything is queued. On any error nothing is
+ *    queued and the outputs are left untouched. A launch failure returns FP4_ERR_HIP; a device
+ *    fault surfaces at the caller's next synchronisation. No C++ exception crosses this ABI.
+ *  - Non-finite inputs are outside the contract: kernels do not fault, results are unspecified.
+ *
+ * Layouts:
+ *  - x / y: row-major [rows, cols] with leading dimension ld (elements), fp32 or bf16.
+ *  - codes: E2M1 -> [rows, cols/2] bytes, element 2j in the low nibble of byte j, bit 3 of a
+ *    nibble is the sign; E4M3 -> [rows, cols] bytes. Contiguous.
+ *  - scales: row-major [rows/block_rows, cols/block_cols]; one byte per block (E8M0 code k+127,
+ *    or an E4M3 code in the NVFP4 modes), or one fp32 per block in FP4_SCALE_F32. Contiguous.
+ *  - tensor_scale: one fp32 (NVFP4 modes only), written by fp4_quantize, read by the others.
+ *  - The quantization axis is always the contiguous `cols` axis (K for GEMM operands).
+ */
+#ifndef BGF_FP4_H
+#define BGF_FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4_ABI_VERSION 1
+
+typedef enum {
+    FP4_OK = 0,
+    FP4_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, sizes that do not tile */
+    FP4_ERR_UNSUPPORTED = 2,  /* a valid combination this library does not implement */
+    FP4_ERR_ALIGNMENT = 3,    /* a device pointer or row pitch not aligned to 16 bytes */
+    FP4_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the size query returned */
+    FP4_ERR_HIP = 5,          /* the HIP runtime rejected a launch */
+    FP4_ERR_INTERNAL = 6
+} fp4_status;
+
+enum { FP4_DT_F32 = 0, FP4_DT_BF16 = 1 };
+enum { FP4_ELEM_E2M1 = 0, FP4_ELEM_E4M3 = 1 };
+enum {
+    FP4_SCALE_E8M0_FLOOR = 0, /* 2^(floor(log2 amax) - emax): emax 2 for E2M1 (6 = 1.5*2^2),
+                                  8 for E4M3 (448 = 1.75*2^8); values above the grid saturate */
+    FP4_SCALE_E8M0_CEIL = 1,  /* truncation-free: the smallest 2^k with maxval * 2^k >= amax */
+    FP4_SCALE_NV = 2,         /* NVFP4: s = E4M3(amax_b / (6 g)), g = amax_tensor / (6 * 448) */
+    FP4_SCALE_NV_4OVER6 = 3,  /* NVFP4, per block the better of the maps amax->6 and amax->4 */
+    FP4_SCALE_F32 = 4         /* fp32 S = amax / maxval (per tensor / per row / per group) */
+};
+enum { FP4_ROUND_RNE = 0, FP4_ROUND_SR = 1 };
+
+/* How a tensor is quantized.
+ *  elem        FP4_ELEM_E2M1 or FP4_ELEM_E4M3.
+ *  block_rows, block_cols
+ *              (1, 32) MX groups; (1, 16) NVFP4 blocks (also allowed for E8M0 / F32 scales);
+ *              (32, 32) 2D tiles (E8M0 scales); (1, cols) per row; (rows, cols) per tensor.
+ *  scale_mode  FP4_SCALE_*.
+ *  round_mode  FP4_ROUND_RNE (ties to even, saturating) or FP4_ROUND_SR (stochastic rounding).
+ *  hadamard_n  0 (no rotation) or 16, 32, 64, 128, 256: rotate each contiguous n-chunk of a row
+ *              by H_n / sqrt(n) (Sylvester order) before quantizing; n must divide cols.
+ *  seed        Philox4x32-10 key for SR. Element (r, c) draws the 16-bit uniform
+ *              u = half (idx & 1) of word (idx >> 1) & 3 of Philox(counter = idx >> 3, key = seed),
+ *              idx = r * cols + c, and rounds up iff u < p * 2^16 where p is its position between
+ *              the two neighbouring grid values. Results are reproducible for a given seed. */
+typedef struct fp4_qparams {
+    int32_t elem;
+    int32_t block_rows;
+    int32_t block_cols;
+    int32_t scale_mode;
+    int32_t round_mode;
+    int32_t hadamard_n;
+    uint64_t seed;
+} fp4_qparams;
+
+/* A quantized tensor as the GEMM reads (A, B) or writes (C_q) it. codes / scales / tensor_scale are
+ * device pointers with the layouts above; rows x cols is the logical shape (cols = K for GEMM
+ * operands); p describes how it was quantized. */
+typedef struct fp4_qtensor {
+    void* codes;
+    void* scales;
+    float* tensor_scale;
+    int64_t rows;
+    int64_t cols;
+    fp4_qparams p;
+} fp4_qtensor;
+
+int fp4_abi_version(void);
+const char* fp4_status_string(int status);
+
+/* Byte sizes of the codes / scales buffers for a rows x cols tensor quantized with *p, and of the
+ * device workspace fp4_quantize needs (0, or 256 for the modes that first take a tensor-wide
+ * amax: NVFP4 and per-tensor blocks). Return -1 for arguments fp4_quantize would reject. */
+int64_t fp4_codes_bytes(int64_t rows, int64_t cols, const fp4_qparams* p);
+int64_t fp4_scales_bytes(int64_t rows, int64_t cols, const fp4_qparams* p);
+int64_t fp4_workspace_bytes(int64_t rows, int64_t cols, const fp4_qparams* p);
+
+/* Quantize x [rows, cols] (x_dtype FP4_DT_F32 / FP4_DT_BF16, leading dimension ldx >= cols) into
+ * codes / scales (and tensor_scale for NVFP4) as described by *p. Per block: rotate (if
+ * hadamard_n), take amax = max |x| over the block, encode the scale, then each element
+ * v = x * RN(1/d) (d the decoded scale; exactly x / d for power-of-two scales) is rounded to the
+ * element grid. Requirements: cols even for E2M1; blocks tile the tensor; 1D groups and 2D tiles
+ * need cols % 32 == 0 (and rows % 32 == 0 for 2D); per-row / per-tensor blocks take no rotation;
+ * SR is not combined with 4/6; x and ldx * element size 16-byte aligned; codes 16-byte aligned.
+ * workspace: device memory of fp4_workspace_bytes() bytes (may be NULL when that is 0). */
+int fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                 const fp4_qparams* p, void* codes, void* scales, float* tensor_scale,
+                 void* workspace, int64_t ws_bytes, void* stream);
+
+/* y = RN(val(q) * d) for every element (d the decoded block scale: 2^k, the fp32 scale, or
+ * RN(E4M3(s) * g) in the NVFP4 modes), then the rotation again when p->hadamard_n > 0 (H/sqrt(n)
+ * is its own inverse). y: [rows, cols] fp32 or bf16 (round to nearest even), leading dim ldy. */
+int fp4_dequantize(const void* codes, const void* scales, const float* tensor_scale, int64_t rows,
+                   int64_t cols, const fp4_qparams* p, void* y, int32_t y_dtype, int64_t ldy,
+                   void* stream);
+
+/* The rotation alone: y [rows, cols] = x with each n-chunk of every row multiplied by H_n/sqrt(n),
+ * fp32 out (the same arithmetic fp4_quantize applies before it quantizes). */
+int fp4_hadamard(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                 int32_t hadamard_n, float* y, void* stream);
+
+/* C [M, N] = A [M, K] * B [N, K]^T on the quantized operands, fp32 accumulation; C fp32 or bf16
+ * (round to nearest even) with leading dimension ldc >= N. Supported operand pairs:
+ * MXFP4 x MXFP4 (E2M1, E8M0 (1, 32) groups; B may use (32, 32) 2D tiles), MXFP8 x MXFP8 (E4M3,
+ * E8M0 (1, 32)), and NVFP4 x NVFP4 (E2M1, (1, 16) NV or 4/6 scales: each 32-wide K group is
+ * re-expressed as E4M3 elements under one power-of-two scale and multiplied on the FP8 matrix
+ * cores, and the product of the two tensor scales is applied in the epilogue).
+ * K % 128 == 0. Operands must not be rotated differently: a rotation along K cancels in A B^T
+ * only when both were rotated with the same n, which the caller ensures.
+ * Optional fused output quantization: if out_q is non-NULL, C_q receives the fp32 result
+ * quantized along N with *out_q (E2M1 or E4M3 elements, E8M0 floor/ceil, (1, 32) groups, RNE or
+ * SR, no rotation); C may then be NULL. workspace: fp4_gemm_workspace_bytes() bytes. */
+int64_t fp4_gemm_workspace_bytes(const fp4_qtensor* A, const fp4_qtensor* B);
+int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtype, int64_t ldc,
+             const fp4_qparams* out_q, fp4_qtensor* C_q, void* workspace, int64_t ws_bytes,
+             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,144 @@
+"""CPU checks of the C ABI library: it loads without a GPU, exports every entry point the header
+declares, and rejects bad arguments on the host before touching the device. Also checks that the
+oracle and the HIP path share no code."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def fp4():
+    from bit_gemm_fwht_amd import fp4 as m
+    if not os.path.exists(m.LIB_PATH):
+        from bit_gemm_fwht_amd import build
+        build.build()
+    m.lib()
+    return m
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "fp4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(fp4):
+    names = _declared()
+    assert {"fp4_quantize", "fp4_dequantize", "fp4_gemm", "fp4_hadamard"} <= set(names)
+    L = fp4.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.fp4_abi_version() == 1
+
+
+def test_status_strings(fp4):
+    for s in range(7):
+        assert fp4.status_string(s)
+
+
+def P(fp4, **kw):
+    base = dict(elem=0, block_rows=1, block_cols=32, scale_mode=0, round_mode=0, hadamard_n=0, seed=0)
+    base.update(kw)
+    return fp4.QParams(**base)
+
+
+def test_size_queries(fp4):
+    L = fp4.lib()
+    p = P(fp4)
+    assert L.fp4_codes_bytes(4096, 4096, ctypes.byref(p)) == 4096 * 2048
+    assert L.fp4_scales_bytes(4096, 4096, ctypes.byref(p)) == 4096 * 128
+    assert L.fp4_workspace_bytes(4096, 4096, ctypes.byref(p)) == 0
+    nv = P(fp4, block_cols=16, scale_mode=3)
+    assert L.fp4_scales_bytes(64, 256, ctypes.byref(nv)) == 64 * 16
+    assert L.fp4_workspace_bytes(64, 256, ctypes.byref(nv)) == 256
+    p2d = P(fp4, block_rows=32, scale_mode=1)
+    assert L.fp4_scales_bytes(4096, 4096, ctypes.byref(p2d)) == 128 * 128
+    f8 = P(fp4, elem=1)
+    assert L.fp4_codes_bytes(8, 64, ctypes.byref(f8)) == 8 * 64
+    f32s = P(fp4, block_rows=256, block_cols=784, scale_mode=4)
+    assert L.fp4_scales_bytes(256, 784, ctypes.byref(f32s)) == 4
+    # rejected shapes
+    assert L.fp4_codes_bytes(4, 33, ctypes.byref(p)) == -1            # cols % 32
+    assert L.fp4_codes_bytes(4, 64, ctypes.byref(P(fp4, hadamard_n=48))) == -1
+    assert L.fp4_codes_bytes(4, 64, ctypes.byref(P(fp4, block_rows=32))) == -1  # rows % 32
+    assert L.fp4_codes_bytes(0, 64, ctypes.byref(p)) == -1
+
+
+def _quant(fp4, p, rows=64, cols=256, x=0x1000, codes=0x2000, scales=0x3000, ts=None, ws=None,
+           wsb=0, ldx=None, dtype=1):
+    return fp4.lib().fp4_quantize(x, dtype, rows, cols, ldx or cols, ctypes.byref(p), codes, scales,
+                                  ts, ws, wsb, None)
+
+
+def test_quantize_validation_without_device(fp4):
+    """Every one of these returns before any HIP call (the pointers are never touched)."""
+    E = fp4
+    assert _quant(fp4, P(fp4), x=None) == E.ERR_INVALID_ARG
+    assert _quant(fp4, P(fp4), codes=None) == E.ERR_INVALID_ARG
+    assert _quant(fp4, P(fp4), cols=250) == E.ERR_INVALID_ARG
+    assert _quant(fp4, P(fp4, elem=7)) == E.ERR_INVALID_ARG
+    assert _quant(fp4, P(fp4, scale_mode=9)) == E.ERR_INVALID_ARG
+    assert _quant(fp4, P(fp4, round_mode=3)) == E.ERR_INVALID_ARG
+    assert _quant(fp4, P(fp4, hadamard_n=512)) == E.ERR_INVALID_ARG
+    assert _quant(fp4, P(fp4, hadamard_n=128), cols=320) == E.ERR_INVALID_ARG
+    assert _quant(fp4, P(fp4, block_cols=64)) == E.ERR_UNSUPPORTED
+    assert _quant(fp4, P(fp4, scale_mode=3, round_mode=1, block_cols=16), ts=0x4000, ws=0x5000,
+                  wsb=256) == E.ERR_UNSUPPORTED                       # SR with 4/6
+    assert _quant(fp4, P(fp4, scale_mode=2)) == E.ERR_UNSUPPORTED        # NV needs 16-blocks
+    assert _quant(fp4, P(fp4, scale_mode=2, block_cols=16)) == E.ERR_INVALID_ARG  # no tensor_scale
+    assert _quant(fp4, P(fp4, scale_mode=2, block_cols=16), ts=0x4000) == E.ERR_WORKSPACE
+    assert _quant(fp4, P(fp4, scale_mode=2, block_cols=16), ts=0x4000, ws=0x5000, wsb=8) == E.ERR_WORKSPACE
+    assert _quant(fp4, P(fp4, block_rows=32, scale_mode=4)) == E.ERR_UNSUPPORTED  # 2D needs E8M0
+    assert _quant(fp4, P(fp4, block_rows=64, block_cols=256, hadamard_n=16)) == E.ERR_UNSUPPORTED
+    assert _quant(fp4, P(fp4), x=0x1004) == E.ERR_ALIGNMENT
+    assert _quant(fp4, P(fp4), codes=0x2008) == E.ERR_ALIGNMENT
+    assert _quant(fp4, P(fp4), ldx=260) == E.ERR_ALIGNMENT             # pitch not 16-B aligned
+    assert _quant(fp4, P(fp4), ldx=100) == E.ERR_INVALID_ARG           # ldx < cols
+    assert _quant(fp4, P(fp4), codes=0x1000) == E.ERR_INVALID_ARG      # aliasing
+
+
+def test_gemm_validation_without_device(fp4):
+    E = fp4
+    L = fp4.lib()
+
+    def qt(rows, cols, **kw):
+        return fp4.QTensorC(0x10000, 0x20000, None, rows, cols, P(fp4, **kw))
+
+    a, b = qt(256, 256), qt(128, 256)
+    c = 0x30000
+    assert L.fp4_gemm(ctypes.byref(a), None, c, 0, 128, None, None, None, 0, None) == E.ERR_INVALID_ARG
+    bk = qt(128, 384)
+    assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(bk), c, 0, 128, None, None, None, 0, None) == E.ERR_INVALID_ARG
+    a96, b96 = qt(256, 96), qt(128, 96)
+    assert L.fp4_gemm(ctypes.byref(a96), ctypes.byref(b96), c, 0, 128, None, None, None, 0, None) == E.ERR_UNSUPPORTED
+    b8 = qt(128, 256, elem=1)
+    assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(b8), c, 0, 128, None, None, None, 0, None) == E.ERR_UNSUPPORTED
+    brot = qt(128, 256, hadamard_n=128)
+    assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(brot), c, 0, 128, None, None, None, 0, None) == E.ERR_INVALID_ARG
+    assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(b), c, 0, 64, None, None, None, 0, None) == E.ERR_INVALID_ARG
+    assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(b), 0x30004, 0, 128, None, None, None, 0, None) == E.ERR_ALIGNMENT
+    an = fp4.QTensorC(0x10000, 0x20000, 0x40000, 256, 256, P(fp4, block_cols=16, scale_mode=3))
+    bn = fp4.QTensorC(0x50000, 0x60000, 0x70000, 128, 256, P(fp4, block_cols=16, scale_mode=2))
+    assert L.fp4_gemm_workspace_bytes(ctypes.byref(an), ctypes.byref(bn)) > 0
+    assert L.fp4_gemm(ctypes.byref(an), ctypes.byref(bn), c, 0, 128, None, None, None, 0, None) == E.ERR_WORKSPACE
+
+
+def test_oracle_and_hip_path_share_no_code():
+    prod = os.path.join(ROOT, "bit_gemm_fwht_amd")
+    orc = os.path.join(ROOT, "oracle")
+    for d, banned in ((orc, ("bit_gemm_fwht_amd", "csrc", "fp4.h", "device.h")),
+                      (prod, ("oracle", "liboracle"))):
+        for dirpath, _, files in os.walk(d):
+            for f in files:
+                if not f.endswith((".c", ".h", ".cpp", ".hip", ".py")):
+                    continue
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                for line in text.splitlines():
+                    s = line.strip()
+                    if s.startswith(("#include", "import ", "from ")):
+                        for b in banned:
+                            assert b not in s, f"{f}: {s}"

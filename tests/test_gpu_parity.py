@@ -1,0 +1,289 @@
+"""GPU parity: the HIP path (called through the C ABI) against the CPU oracle on the same seeded
+inputs. Codes, scales and tensor scales must be bit-identical (stochastic rounding included);
+dequantized values and rotations bit-identical; GEMM outputs within
+|C - C_ref| <= 1e-5 * sum_k |a_k b_k| (+ half a bf16 ulp of C_ref for bf16 outputs)."""
+import numpy as np
+import pytest
+import torch
+
+from bit_gemm_fwht_amd import fp4
+from bit_gemm_fwht_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _to_dev(x: np.ndarray) -> torch.Tensor:
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+
+
+def _gpu_quant(x: np.ndarray, params: fp4.Params):
+    xt = _to_dev(x)
+    q = fp4.quantize(xt, params)
+    torch.cuda.synchronize()
+    codes = q.codes.cpu().numpy()
+    scales = q.scales.cpu().numpy()
+    ts = q.tensor_scale.cpu().numpy() if q.tensor_scale is not None else None
+    return q, codes, scales, ts
+
+
+def _orc_quant(orc, x, params: fp4.Params):
+    return orc.quantize(x, elem=params.elem, block=params.block, scale_mode=params.scale_mode,
+                        round_mode=params.round_mode, hadamard_n=params.hadamard_n, seed=params.seed)
+
+
+def _check_quant(orc, x, params, check_dequant=True):
+    q, gc, gs, gts = _gpu_quant(x, params)
+    oc, os_, ots = _orc_quant(orc, x, params)
+    oc = oc.reshape(-1)
+    os_ = os_.reshape(-1).view(np.uint8)
+    assert gc.shape == oc.shape and gs.shape == os_.shape
+    bad = np.nonzero(gc != oc)[0]
+    assert bad.size == 0, f"{bad.size} code bytes differ, first at {bad[:8]}: gpu {gc[bad[:8]]} oracle {oc[bad[:8]]}"
+    bad = np.nonzero(gs != os_)[0]
+    assert bad.size == 0, f"{bad.size} scale bytes differ, first at {bad[:8]}: gpu {gs[bad[:8]]} oracle {os_[bad[:8]]}"
+    if ots is not None:
+        assert gts.view(np.uint32)[0] == ots.view(np.uint32)[0]
+    if check_dequant:
+        rows, cols = x.shape
+        oc2, os2, ots2 = _orc_quant(orc, x, params)
+        ref = orc.dequantize(oc2, os2, ots2, rows, cols, elem=params.elem, block=params.block,
+                             scale_mode=params.scale_mode, hadamard_n=params.hadamard_n)
+        for dt in (torch.float32, torch.bfloat16):
+            y = fp4.dequantize(q, dtype=dt)
+            torch.cuda.synchronize()
+            if dt == torch.float32:
+                got = y.cpu().numpy()
+                bad = np.nonzero(got.view(np.uint32) != ref.view(np.uint32))
+                assert bad[0].size == 0, f"dequant differs at {bad[0][:4]}, {bad[1][:4]}"
+            else:
+                got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+                assert np.array_equal(got, orc.bf16_rne(ref))
+    return q
+
+
+def _mix(rows, cols, seed, dtype="bf16", scale=1.0):
+    """N(0, scale^2) with a few outliers, exact midpoints, zeros and tiny values mixed in."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((rows, cols)) * scale).astype(np.float32)
+    flat = x.reshape(-1)
+    n = flat.size
+    idx = rng.choice(n, size=max(n // 50, 1), replace=False)
+    flat[idx[: len(idx) // 4]] *= 40
+    flat[idx[len(idx) // 4: len(idx) // 2]] = 0.0
+    flat[idx[len(idx) // 2: 3 * len(idx) // 4]] = -0.0
+    flat[idx[3 * len(idx) // 4:]] = rng.choice(np.float32([0.25, 0.75, 1.25, 2.5, 3.5, 5.0, 1e-39, -1e-42]),
+                                               size=len(idx) - 3 * len(idx) // 4)
+    if dtype == "bf16":
+        return wl.f32_to_bf16_bits(x)
+    return x
+
+
+P = fp4.Params
+E2M1, E4M3 = fp4.E2M1, fp4.E4M3
+FLOOR, CEIL, NV, NV46, F32 = (fp4.SCALE_E8M0_FLOOR, fp4.SCALE_E8M0_CEIL, fp4.SCALE_NV,
+                              fp4.SCALE_NV_4OVER6, fp4.SCALE_F32)
+RNE, SR = fp4.ROUND_RNE, fp4.ROUND_SR
+
+
+# ---------------------------------------------------------------------------------------------
+# quantize / dequantize parity
+# ---------------------------------------------------------------------------------------------
+def test_tiny_mxfp4_check(orc):
+    """Tiny MXFP4 check: A, B 256x256 N(0,1) with a 50x outlier in A; group 32, E8M0 floor, RNE."""
+    a, b = wl.tiny_mxfp4(0)
+    _check_quant(orc, a, P())
+    _check_quant(orc, b, P())
+    # per-tensor S = amax / 6 on A: the outlier collapse
+    q = _check_quant(orc, a, P(block=a.shape, scale_mode=F32))
+    codes = q.codes.cpu().numpy()
+    nz = np.count_nonzero(codes & 0x7) + np.count_nonzero((codes >> 4) & 0x7)
+    assert nz == 1
+
+
+SEG_CASES = []
+for dt in ("bf16", "f32"):
+    for hn in (0, 16, 32, 64, 128, 256):
+        for elem in (E2M1, E4M3):
+            for sm in (FLOOR, CEIL):
+                for rnd in (RNE, SR):
+                    SEG_CASES.append((dt, hn, elem, sm, rnd))
+
+
+@pytest.mark.parametrize("dt,hn,elem,sm,rnd", SEG_CASES)
+def test_group32_parity(orc, dt, hn, elem, sm, rnd):
+    # 37 rows x 512 columns = 592 lanes: three workgroups, the last one ragged
+    x = _mix(37, 512, seed=hn + 7 * elem + 13 * sm + 29 * rnd, dtype=dt)
+    _check_quant(orc, x, P(elem=elem, scale_mode=sm, round_mode=rnd, hadamard_n=hn, seed=12345))
+
+
+@pytest.mark.parametrize("elem,sm,rnd,hn", [(E2M1, FLOOR, RNE, 0), (E2M1, CEIL, SR, 128),
+                                            (E4M3, FLOOR, RNE, 64), (E2M1, F32, RNE, 0),
+                                            (E2M1, F32, SR, 32), (E4M3, F32, RNE, 256)])
+def test_group16_and_f32_scales(orc, elem, sm, rnd, hn):
+    x = _mix(40, 768, seed=3, dtype="bf16")
+    _check_quant(orc, x, P(elem=elem, block=(1, 16), scale_mode=sm, round_mode=rnd, hadamard_n=hn, seed=9))
+    _check_quant(orc, x, P(elem=elem, block=(1, 32), scale_mode=sm, round_mode=rnd, hadamard_n=hn, seed=9))
+
+
+@pytest.mark.parametrize("cols", [512, 288])
+@pytest.mark.parametrize("elem,sm,rnd,hn", [(E2M1, FLOOR, RNE, 0), (E2M1, CEIL, RNE, 32),
+                                            (E2M1, CEIL, SR, 0), (E4M3, CEIL, SR, 32),
+                                            (E2M1, CEIL, RNE, 128)])
+def test_2d_parity(orc, cols, elem, sm, rnd, hn):
+    if cols % max(hn, 1):
+        pytest.skip("rotation size does not divide the width")
+    x = _mix(96, cols, seed=5, dtype="bf16", scale=0.02)
+    _check_quant(orc, x, P(elem=elem, block=(32, 32), scale_mode=sm, round_mode=rnd, hadamard_n=hn, seed=7))
+
+
+@pytest.mark.parametrize("sm,rnd,hn", [(NV, RNE, 0), (NV46, RNE, 0), (NV, SR, 0), (NV46, RNE, 128),
+                                        (NV, RNE, 64)])
+def test_nvfp4_parity(orc, sm, rnd, hn):
+    x, _ = wl.nvfp4_4over6(0, m=48, n=16, k=1024)
+    _check_quant(orc, x, P(block=(1, 16), scale_mode=sm, round_mode=rnd, hadamard_n=hn, seed=3))
+
+
+@pytest.mark.parametrize("outlier", [False, True])
+@pytest.mark.parametrize("elem,sm,rnd", [(E2M1, F32, RNE), (E2M1, FLOOR, RNE), (E2M1, CEIL, SR),
+                                         (E4M3, FLOOR, RNE), (E4M3, F32, SR)])
+def test_mnist_mlp_granularities(orc, outlier, elem, sm, rnd):
+    """MNIST-MLP-shaped weights: per-tensor, per-row and flattened group-32 scales."""
+    w = wl.mnist_mlp(0, outlier=outlier)
+    for name, x in w.items():
+        rows, cols = x.shape
+        _check_quant(orc, x, P(elem=elem, block=(rows, cols), scale_mode=sm, round_mode=rnd, seed=1))
+        _check_quant(orc, x, P(elem=elem, block=(1, cols), scale_mode=sm, round_mode=rnd, seed=1))
+        flat = x.reshape(1, -1)
+        _check_quant(orc, flat, P(elem=elem, block=(1, 32), scale_mode=sm, round_mode=rnd, seed=1))
+
+
+def test_degenerate_inputs(orc):
+    z = np.zeros((32, 256), dtype=np.float32)
+    z[1, ::2] = -0.0
+    for params in (P(), P(scale_mode=CEIL, round_mode=SR), P(block=(1, 16), scale_mode=NV46),
+                   P(block=(32, 32)), P(elem=E4M3), P(block=(32, 256), scale_mode=F32),
+                   P(hadamard_n=256)):
+        _check_quant(orc, z, params)
+    tiny = np.full((32, 256), 1e-40, dtype=np.float32)
+    tiny[:, ::3] = -3e-39
+    tiny[:, 1::7] = 1e-45
+    for params in (P(), P(scale_mode=CEIL), P(elem=E4M3), P(scale_mode=CEIL, round_mode=SR),
+                   P(block=(1, 16), scale_mode=NV)):
+        _check_quant(orc, tiny, params)
+    big = np.full((32, 256), 3e38, dtype=np.float32)
+    big[:, ::2] = -1.7e38
+    for params in (P(), P(scale_mode=CEIL), P(elem=E4M3, scale_mode=CEIL)):
+        _check_quant(orc, big, params)
+    one = _mix(1, 32, seed=1, dtype="f32")
+    _check_quant(orc, one, P())
+
+
+def test_hadamard_parity(orc):
+    for hn in (16, 32, 64, 128, 256):
+        x = _mix(19, 1024, seed=hn, dtype="f32")
+        y = fp4.hadamard(_to_dev(x), hn)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), orc.fwht(x, hn).view(np.uint32))
+        xb = _mix(19, 1024, seed=hn, dtype="bf16")
+        y = fp4.hadamard(_to_dev(xb), hn)
+        ref = orc.fwht(wl.bf16_bits_to_f32(xb).reshape(19, 1024), hn)
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_sr_seed_reproducible_and_distinct():
+    x = _to_dev(_mix(64, 512, seed=2, dtype="bf16"))
+    p = P(scale_mode=CEIL, round_mode=SR, seed=7)
+    a = fp4.quantize(x, p).codes.cpu().numpy()
+    b = fp4.quantize(x, p).codes.cpu().numpy()
+    c = fp4.quantize(x, P(scale_mode=CEIL, round_mode=SR, seed=8)).codes.cpu().numpy()
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
+
+
+# ---------------------------------------------------------------------------------------------
+# GEMM parity
+# ---------------------------------------------------------------------------------------------
+def _gemm_check(orc, A, B, params_a, params_b, c_dtype=torch.float32, sample=None):
+    """Quantize on the oracle, upload, multiply on the GPU, compare with the fp64 reference."""
+    M, K = A.shape
+    N = B.shape[0]
+    ca, sa, ta = _orc_quant(orc, A, params_a)
+    cb, sb, tb = _orc_quant(orc, B, params_b)
+    qa = fp4.upload_qtensor(ca, sa, ta, M, K, params_a, DEV)
+    qb = fp4.upload_qtensor(cb, sb, tb, N, K, params_b, DEV)
+    c = fp4.gemm(qa, qb, out_dtype=c_dtype)
+    torch.cuda.synchronize()
+    got = c.float().cpu().numpy().astype(np.float64)
+    kw_a = dict(elem=params_a.elem, block=params_a.block, scale_mode=params_a.scale_mode)
+    kw_b = dict(elem=params_b.elem, block=params_b.block, scale_mode=params_b.scale_mode)
+    if sample is None:
+        a64 = orc.operand_f64(ca, sa, ta, M, K, **kw_a)
+        b64 = orc.operand_f64(cb, sb, tb, N, K, **kw_b)
+        ref, sabs = orc.gemm_f64(a64, b64)
+        g = got
+    else:
+        ms, ns = sample
+        ur, inv_m = np.unique(ms, return_inverse=True)
+        un, inv_n = np.unique(ns, return_inverse=True)
+        ca_r = ca[ur]
+        sa_r = sa[ur] if params_a.block[0] == 1 else None
+        cb_r = cb[un]
+        sb_r = sb[un] if params_b.block[0] == 1 else sb[un // 32]
+        a64 = orc.operand_f64(ca_r, sa_r, ta, len(ur), K, **kw_a)
+        if params_b.block[0] == 1:
+            b64 = orc.operand_f64(cb_r, sb_r, tb, len(un), K, **kw_b)
+        else:  # 2D scales: expand the sampled rows' tile scales to per-row groups
+            kw1 = dict(kw_b, block=(1, 32))
+            b64 = orc.operand_f64(cb_r, np.ascontiguousarray(sb_r), tb, len(un), K, **kw1)
+        ref, sabs = orc.gemm_f64_sampled(a64, b64, inv_m, inv_n)
+        g = got[ms, ns]
+    tol = 1e-5 * sabs
+    fp8_core = params_a.elem == E4M3 or params_a.scale_mode in (NV, NV46)
+    if fp8_core:
+        # The FP8 matrix core aligns the 128 products of one instruction to the largest of them and
+        # keeps 13 bits below its leading bit (truncating toward zero): each instruction may lose
+        # up to 128 * 2^(e - 13), e = floor(log2 max |a_k b_k|) over its 128-wide K slice.
+        if sample is None:
+            prod_max = np.stack([np.abs(a64[:, None, s:s + 128] * b64[None, :, s:s + 128]).max(axis=2)
+                                 for s in range(0, K, 128)], axis=-1)
+        else:
+            prod_max = np.stack([np.abs(a64[inv_m, s:s + 128] * b64[inv_n, s:s + 128]).max(axis=1)
+                                 for s in range(0, K, 128)], axis=-1)
+        with np.errstate(divide="ignore"):
+            e = np.floor(np.log2(np.where(prod_max > 0, prod_max, 1.0)))
+        tol = tol + np.where(prod_max > 0, 128.0 * 2.0 ** (e - 13), 0.0).sum(axis=-1)
+    if c_dtype == torch.bfloat16:
+        tol = tol + np.abs(ref) * 2.0**-8 + 1e-38  # half a bf16 ulp is at most 2^-8 |ref|
+    err = np.abs(g - ref)
+    worst = np.argmax(err - tol)
+    assert np.all(err <= tol), f"max excess at {worst}: err {err.flat[worst]} tol {tol.flat[worst]} ref {ref.flat[worst]}"
+    return c
+
+
+def test_gemm_tiny_mxfp4(orc):
+    a, b = wl.tiny_mxfp4(0)
+    _gemm_check(orc, a, b, P(), P())
+    _gemm_check(orc, a, b, P(), P(), c_dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 136, 384), (1, 1, 128), (129, 257, 256), (64, 300, 512)])
+@pytest.mark.parametrize("kind", ["mxfp4", "mxfp4_2d", "mxfp8", "nvfp4"])
+def test_gemm_shapes(orc, M, N, K, kind):
+    rng = np.random.default_rng(M + N + K)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    if kind == "mxfp4":
+        pa, pb = P(), P(scale_mode=CEIL)
+    elif kind == "mxfp4_2d":
+        if N % 32:
+            pytest.skip("2D tiles need N % 32 == 0")
+        pa, pb = P(), P(block=(32, 32), scale_mode=CEIL)
+    elif kind == "mxfp8":
+        pa, pb = P(elem=E4M3), P(elem=E4M3, scale_mode=CEIL)
+    else:
+        pa, pb = P(block=(1, 16), scale_mode=NV46), P(block=(1, 16), scale_mode=NV)
+    _gemm_check(orc, A, B, pa, pb)
+    _gemm_check(orc, A, B, pa, pb, c_dtype=torch.bfloat16)
