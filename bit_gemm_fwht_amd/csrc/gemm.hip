@@ -175,6 +175,240 @@ __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Large-tile pipelined kernel: 256 x 256 workgroup tile, 4 waves of 128 x 128, 32x32x64 scaled
+// MFMAs (lane l: row l % 32, 32 K values of group l / 32 of the instruction's 64; result lane l,
+// register i: D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32]).
+// A multi-stage LDS ring is filled by direct global->LDS 128-bit loads (no VGPR staging): each
+// wave writes 1 KB contiguous blocks, so a row's 16-byte chunks are placed by choosing which
+// chunk each lane fetches. The chunk slot is XOR-swizzled with bits of the row so that the
+// 16-byte fragment reads of consecutive rows hit distinct LDS banks (for 32 and 64 banks).
+// Scales: one dword (4 K groups) per row per 128-deep step, shifted per lane so that a fixed
+// OPSEL byte selects the lane's group.
+// Workgroups are renumbered so that each of the 8 XCDs (which receive workgroup ids round-robin)
+// owns a contiguous run of tiles, walked in groups of 4 tile rows for L2 reuse.
+// ---------------------------------------------------------------------------------------------
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <bool FP8>
+struct Big {
+    static constexpr int TM = 256, TN = 256;
+    static constexpr int RB = FP8 ? 128 : 64;         // bytes per row per 128-deep K step
+    static constexpr int CPR = RB / 16;               // 16-byte chunks per row
+    static constexpr int NST = FP8 ? 2 : 3;           // pipeline stages
+    static constexpr int OPB = TM * RB;               // operand bytes per stage
+    static constexpr int STAGE = 2 * OPB + 2 * 4 * TM;
+    static constexpr int IPW = OPB / 1024 / 4;        // 1 KB load instructions per wave per operand
+    static constexpr int LOADS = 2 * IPW + 2;         // vector-memory instructions per thread per stage
+};
+
+template <bool FP8>
+__device__ __forceinline__ int chunk_swz(int r) {
+    if constexpr (FP8) return (r & 7) ^ ((r >> 3) & 1);
+    return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
+}
+
+__device__ __forceinline__ void wait_vm(int n) {
+    // gfx9 s_waitcnt: vmcnt in bits [3:0] and [15:14]; expcnt / lgkmcnt left at their maximum
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+        case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+        case 18: __builtin_amdgcn_s_waitcnt(0x4F72); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+}
+
+template <bool FP8, bool B2D, int OUT, bool NVG>
+__global__ __launch_bounds__(256) void k_gemm_big(GemmArgs g) {
+    using C = Big<FP8>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // tile assignment: XCD-contiguous runs, grouped by 4 tile rows
+    const int ntm = (int)((g.M + C::TM - 1) / C::TM), ntn = (int)((g.N + C::TN - 1) / C::TN);
+    const int T = ntm * ntn;
+    int b = blockIdx.x;
+    if (T % 8 == 0) b = (b % 8) * (T / 8) + b / 8;
+    const int GM = 4;
+    const int grp = b / (GM * ntn), first = grp * GM;
+    const int gs = (ntm - first) < GM ? (ntm - first) : GM;
+    const int tm = first + (b % (GM * ntn)) % gs, tn = (b % (GM * ntn)) / gs;
+    const int64_t m0 = (int64_t)tm * C::TM, n0 = (int64_t)tn * C::TN;
+
+    const int64_t rowbytes = FP8 ? g.K : g.K / 2;
+    const int64_t kgroups = g.K / 32;
+    const int KT = (int)(g.K / 128);
+
+    // per-thread global source pointers for the direct-to-LDS copies (rows clamped into range:
+    // rows past M / N only feed outputs that are never stored)
+    const uint8_t* srcA[C::IPW];
+    const uint8_t* srcB[C::IPW];
+#pragma unroll
+    for (int i = 0; i < C::IPW; ++i) {
+        const int u = (wave * C::IPW + i) * 64 + lane;
+        const int r = u / C::CPR, slot = u % C::CPR;
+        const int c = slot ^ chunk_swz<FP8>(r);
+        const int64_t ma = (m0 + r) < g.M ? (m0 + r) : (g.M - 1);
+        const int64_t nb = (n0 + r) < g.N ? (n0 + r) : (g.N - 1);
+        srcA[i] = g.a + ma * rowbytes + 16 * c;
+        srcB[i] = g.b + nb * rowbytes + 16 * c;
+    }
+    const int srow = wave * 64 + lane;
+    const int64_t sam = (m0 + srow) < g.M ? (m0 + srow) : (g.M - 1);
+    int64_t sbn = (n0 + srow) < g.N ? (n0 + srow) : (g.N - 1);
+    if (B2D) sbn >>= 5;
+    const uint8_t* srcSA = g.sa + sam * kgroups;
+    const uint8_t* srcSB = g.sb + sbn * kgroups;
+
+    auto issue = [&](int kt) {
+        uint8_t* st = smem + (kt % C::NST) * C::STAGE;
+#pragma unroll
+        for (int i = 0; i < C::IPW; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(srcA[i] + (int64_t)kt * C::RB),
+                                             (lds_ptr_t)(st + (wave * C::IPW + i) * 1024), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < C::IPW; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(srcB[i] + (int64_t)kt * C::RB),
+                                             (lds_ptr_t)(st + C::OPB + (wave * C::IPW + i) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(srcSA + 4 * kt),
+                                         (lds_ptr_t)(st + 2 * C::OPB + wave * 256), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(srcSB + 4 * kt),
+                                         (lds_ptr_t)(st + 2 * C::OPB + 4 * C::TM + wave * 256), 4, 0, 0);
+    };
+
+    v16f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    const int fr = lane & 31, fg = lane >> 5;
+    // loop-invariant LDS byte offsets of this lane's fragments within a stage:
+    // [kk][i][piece]; FP4 uses one 16-byte piece per fragment, FP8 two
+    constexpr int NP = FP8 ? 2 : 1;
+    int offA[2][4][NP], offB[2][4][NP], offSA[4], offSB[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ra = wm * 128 + 32 * i + fr, rb = wn * 128 + 32 * i + fr;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int c = FP8 ? (4 * kk + 2 * p + fg) : (2 * kk + fg);
+                offA[kk][i][p] = ra * C::RB + 16 * (c ^ chunk_swz<FP8>(ra));
+                offB[kk][i][p] = C::OPB + rb * C::RB + 16 * (c ^ chunk_swz<FP8>(rb));
+            }
+        offSA[i] = 2 * C::OPB + 4 * ra;
+        offSB[i] = 2 * C::OPB + 4 * C::TM + 4 * rb;
+    }
+    const int sshift = 8 * fg;
+
+#pragma unroll
+    for (int s = 0; s < C::NST - 1; ++s)
+        if (s < KT) issue(s);
+
+    auto compute = [&](const uint8_t* st) {
+        int sa[4], sb[4];
+        v8i fa[2][4], fb[2][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sa[i] = (int)(*reinterpret_cast<const uint32_t*>(st + offSA[i]) >> sshift);
+            sb[i] = (int)(*reinterpret_cast<const uint32_t*>(st + offSB[i]) >> sshift);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 xa0 = *reinterpret_cast<const u32x4*>(st + offA[kk][i][0]);
+                const u32x4 xb0 = *reinterpret_cast<const u32x4*>(st + offB[kk][i][0]);
+                if constexpr (!FP8) {
+                    fa[kk][i] = (v8i){(int)xa0[0], (int)xa0[1], (int)xa0[2], (int)xa0[3], 0, 0, 0, 0};
+                    fb[kk][i] = (v8i){(int)xb0[0], (int)xb0[1], (int)xb0[2], (int)xb0[3], 0, 0, 0, 0};
+                } else {
+                    const u32x4 xa1 = *reinterpret_cast<const u32x4*>(st + offA[kk][i][NP - 1]);
+                    const u32x4 xb1 = *reinterpret_cast<const u32x4*>(st + offB[kk][i][NP - 1]);
+                    fa[kk][i] = (v8i){(int)xa0[0], (int)xa0[1], (int)xa0[2], (int)xa0[3],
+                                      (int)xa1[0], (int)xa1[1], (int)xa1[2], (int)xa1[3]};
+                    fb[kk][i] = (v8i){(int)xb0[0], (int)xb0[1], (int)xb0[2], (int)xb0[3],
+                                      (int)xb1[0], (int)xb1[1], (int)xb1[2], (int)xb1[3]};
+                }
+            }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int in = 0; in < 4; ++in)
+#pragma unroll
+                for (int im = 0; im < 4; ++im) {
+                    if (kk == 0)
+                        acc[in][im] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            fb[0][in], fa[0][im], acc[in][im], FP8 ? 0 : 4, FP8 ? 0 : 4, 0, sb[in], 0, sa[im]);
+                    else
+                        acc[in][im] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            fb[1][in], fa[1][im], acc[in][im], FP8 ? 0 : 4, FP8 ? 0 : 4, 2, sb[in], 2, sa[im]);
+                }
+    };
+
+    // main loop, unrolled by the stage count so every stage base is a constant
+    for (int k0 = 0; k0 < KT; k0 += C::NST) {
+#pragma unroll
+        for (int s = 0; s < C::NST; ++s) {
+            const int kt = k0 + s;
+            if (kt < KT) {
+                // stage kt's copies are done once at most the next stage's copies are in flight
+                if (C::NST > 2 && kt + 1 < KT) wait_vm(C::LOADS);
+                else wait_vm(0);
+                __builtin_amdgcn_s_barrier();
+                if (kt + C::NST - 1 < KT) issue(kt + C::NST - 1);
+                compute(smem + s * C::STAGE);
+            }
+        }
+    }
+
+    // epilogue: lane holds, per 4-register group q, C[m][n .. n+3] with m = tile row base + l % 32,
+    // n = tile column base + 8 q + 4 (l / 32)
+    float gscale = 1.0f;
+    if constexpr (NVG) gscale = (*g.ga) * (*g.gb);
+#pragma unroll
+    for (int im = 0; im < 4; ++im) {
+        const int64_t m = m0 + wm * 128 + 32 * im + fr;
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int in = 0; in < 4; ++in)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = n0 + wn * 128 + 32 * in + 8 * q + 4 * fg;
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = NVG ? acc[in][im][4 * q + i] * gscale : acc[in][im][4 * q + i];
+                if constexpr (OUT == DT_F32) {
+                    float* cp = reinterpret_cast<float*>(g.c) + m * g.ldc + n;
+                    if (n + 3 < g.N && ((g.ldc & 3) == 0)) {
+                        *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (n + i < g.N) cp[i] = v[i];
+                    }
+                } else {
+                    uint16_t* cp = reinterpret_cast<uint16_t*>(g.c) + m * g.ldc + n;
+                    if (n + 3 < g.N && ((g.ldc & 3) == 0)) {
+                        const uint32_t w0 = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
+                        const uint32_t w1 = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+                        *reinterpret_cast<uint2*>(cp) = make_uint2(w0, w1);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (n + i < g.N) cp[i] = (uint16_t)bf16_rne_bits(v[i]);
+                    }
+                }
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
 // NVFP4 -> MXFP8 re-expression: one lane per 32-wide K group of one row.
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_nv_to_fp8(const uint8_t* codes, const uint8_t* scales,
@@ -213,6 +447,21 @@ __global__ __launch_bounds__(256) void k_nv_to_fp8(const uint8_t* codes, const u
 
 template <bool FP8, bool B2D, bool NVG>
 static hipError_t launch_out(const GemmArgs& g, int c_dtype, hipStream_t s) {
+    if (g.M >= 256 && g.N >= 256) {
+        using C = Big<FP8>;
+        const unsigned tiles = (unsigned)(((g.M + 255) / 256) * ((g.N + 255) / 256));
+        const size_t lds = (size_t)C::NST * C::STAGE;
+        if (c_dtype == DT_BF16) {
+            auto k = k_gemm_big<FP8, B2D, DT_BF16, NVG>;
+            hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            hipLaunchKernelGGL(k, dim3(tiles), dim3(256), lds, s, g);
+        } else {
+            auto k = k_gemm_big<FP8, B2D, DT_F32, NVG>;
+            hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            hipLaunchKernelGGL(k, dim3(tiles), dim3(256), lds, s, g);
+        }
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM));
     if (c_dtype == DT_BF16) hipLaunchKernelGGL((k_gemm<FP8, B2D, DT_BF16, NVG>), grid, dim3(NT), 0, s, g);
     else hipLaunchKernelGGL((k_gemm<FP8, B2D, DT_F32, NVG>), grid, dim3(NT), 0, s, g);

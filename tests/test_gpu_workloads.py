@@ -1,0 +1,85 @@
+"""Parity at the full sizes of the large workloads, in the configuration bench.py times:
+quantization compared element for element with the oracle (codes and scales bit-exact), GEMM
+outputs compared on a seeded sample of 2048 positions (the oracle computes each one on its own)."""
+import numpy as np
+import pytest
+import torch
+
+from bit_gemm_fwht_amd import fp4
+from bit_gemm_fwht_amd import workloads as wl
+from test_gpu_parity import CEIL, E4M3, NV46, SR, P, _gemm_tol, _orc_quant, _to_dev
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _quant_both(orc, x, params):
+    q = fp4.quantize(_to_dev(x), params)
+    torch.cuda.synchronize()
+    oc, os_, ots = _orc_quant(orc, x, params)
+    assert np.array_equal(q.codes.cpu().numpy(), oc.reshape(-1)), "codes differ from the oracle"
+    assert np.array_equal(q.scales.cpu().numpy(), os_.reshape(-1).view(np.uint8)), "scales differ"
+    if ots is not None:
+        assert q.tensor_scale.cpu().numpy().view(np.uint32)[0] == ots.view(np.uint32)[0]
+    return q, (oc, os_, ots)
+
+
+def _sampled_gemm(orc, qa, qb, oa, ob, pa, pb, c_dtype, n=2048, seed=0):
+    c = fp4.gemm(qa, qb, out_dtype=c_dtype)
+    torch.cuda.synchronize()
+    M, N, K = qa.rows, qb.rows, qa.cols
+    rng = np.random.default_rng(seed)
+    ms = rng.integers(0, M, n)
+    ns = rng.integers(0, N, n)
+    ms[:4] = [0, M - 1, 0, M - 1]
+    ns[:4] = [0, N - 1, N - 1, 0]
+    got = c[torch.from_numpy(ms).to(DEV), torch.from_numpy(ns).to(DEV)].float().cpu().numpy().astype(np.float64)
+    ur, im = np.unique(ms, return_inverse=True)
+    un, inn = np.unique(ns, return_inverse=True)
+    kw_a = dict(elem=pa.elem, block=pa.block, scale_mode=pa.scale_mode)
+    a64 = orc.operand_f64(oa[0][ur], oa[1][ur], oa[2], len(ur), K, **kw_a)
+    if pb.block[0] == 1:
+        b64 = orc.operand_f64(ob[0][un], ob[1][un], ob[2], len(un), K, elem=pb.elem, block=pb.block,
+                              scale_mode=pb.scale_mode)
+    else:
+        b64 = orc.operand_f64(ob[0][un], np.ascontiguousarray(ob[1][un // 32]), ob[2], len(un), K,
+                              elem=pb.elem, block=(1, 32), scale_mode=pb.scale_mode)
+    ref, sabs = orc.gemm_f64_sampled(a64, b64, im, inn)
+    tol = _gemm_tol(ref, sabs, a64, b64, im, inn, pa, K, c_dtype)
+    err = np.abs(got - ref)
+    assert np.all(err <= tol), f"{np.sum(err > tol)} of {n} sampled outputs exceed the bound"
+
+
+def test_llama7b_forward_linear(orc):
+    """X 4096x4096, W 11008x4096 (bf16), H_128 + MXFP4; 4096x11008x4096 GEMM to bf16."""
+    x, w, _ = wl.llama_linear(0)
+    p = P(hadamard_n=128)
+    qx, ox = _quant_both(orc, x, p)
+    qw, ow = _quant_both(orc, w, p)
+    _sampled_gemm(orc, qx, qw, ox, ow, p, p, torch.bfloat16)
+
+
+def test_backward_2d_scales(orc):
+    """W 4096x4096 2D 32x32 truncation-free RNE, dY 8192x4096 group-32 truncation-free SR (seed 7),
+    both rotated by H_128; dX = dY W^T in MXFP4, and the MXFP8 variant."""
+    w, dy = wl.backward_2d(0)
+    pw = P(block=(32, 32), scale_mode=CEIL, hadamard_n=128)
+    pd = P(scale_mode=CEIL, round_mode=SR, hadamard_n=128, seed=7)
+    qw, ow = _quant_both(orc, w, pw)
+    qd, od = _quant_both(orc, dy, pd)
+    _sampled_gemm(orc, qd, qw, od, ow, pd, pw, torch.bfloat16)
+    pw8 = P(elem=E4M3, scale_mode=CEIL, hadamard_n=128)
+    pd8 = P(elem=E4M3, scale_mode=CEIL, round_mode=SR, hadamard_n=128, seed=7)
+    qw8, ow8 = _quant_both(orc, w, pw8)
+    qd8, od8 = _quant_both(orc, dy, pd8)
+    _sampled_gemm(orc, qd8, qw8, od8, ow8, pd8, pw8, torch.bfloat16)
+
+
+def test_nvfp4_4over6(orc):
+    """X 8192x8192 Laplace with 0.1% x30 outliers and W 8192x8192 N(0, 0.02^2), NVFP4 with the
+    4/6 choice; the 8192^3 GEMM through the FP8 re-expression."""
+    x, w = wl.nvfp4_4over6(0)
+    p = P(block=(1, 16), scale_mode=NV46)
+    qx, ox = _quant_both(orc, x, p)
+    qw, ow = _quant_both(orc, w, p)
+    _sampled_gemm(orc, qx, qw, ox, ow, p, p, torch.bfloat16)
