@@ -175,9 +175,10 @@ __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Large-tile pipelined kernel: 256 x 256 workgroup tile, 4 waves of 128 x 128, 32x32x64 scaled
-// MFMAs (lane l: row l % 32, 32 K values of group l / 32 of the instruction's 64; result lane l,
-// register i: D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32]).
+// Large-tile pipelined kernel: 256 x 256 workgroup tile, 8 waves (two per SIMD, so one wave's
+// waits are covered by the other's matrix work), each wave a 128 x 64 quadrant of 4 x 2 tiles of
+// the 32x32x64 scaled MFMA (lane l: row l % 32, 32 K values of group l / 32 of the instruction's
+// 64; result lane l, register i: D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32]).
 // A multi-stage LDS ring is filled by direct global->LDS 128-bit loads (no VGPR staging): each
 // wave writes 1 KB contiguous blocks, so a row's 16-byte chunks are placed by choosing which
 // chunk each lane fetches. The chunk slot is XOR-swizzled with bits of the row so that the
@@ -192,38 +193,46 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <bool FP8>
 struct Big {
-    static constexpr int TM = 256, TN = 256;
-    static constexpr int RB = FP8 ? 128 : 64;         // bytes per row per 128-deep K step
+    static constexpr int TM = 256, TN = 256, NW = 8, NTH = 64 * NW;
+    static constexpr int WTM = 4, WTN = 2;            // 32x32 tiles per wave (M x N)
+    // One stage covers 128 bytes of every row (full 128-byte cache lines): 256 K values of FP4
+    // or 128 of FP8.
+    static constexpr int KSTEP = FP8 ? 128 : 256;
+    static constexpr int RB = 128;                    // bytes per row per stage
     static constexpr int CPR = RB / 16;               // 16-byte chunks per row
-    static constexpr int NST = FP8 ? 2 : 3;           // pipeline stages
+    static constexpr int NKK = KSTEP / 64;            // 64-deep MFMA steps per stage
+    static constexpr int SPR = KSTEP / 32;            // scale bytes per row per stage
+    static constexpr int NST = 2;                     // pipeline stages
     static constexpr int OPB = TM * RB;               // operand bytes per stage
-    static constexpr int STAGE = 2 * OPB + 2 * 4 * TM;
-    static constexpr int IPW = OPB / 1024 / 4;        // 1 KB load instructions per wave per operand
-    static constexpr int LOADS = 2 * IPW + 2;         // vector-memory instructions per thread per stage
+    static constexpr int SB = TM * SPR;               // scale bytes per operand per stage
+    // stage layout: A's scales, B's scales, A's codes, B's codes (scales first, so that the
+    // scale reads of a stage reach every tile with one base register and 16-bit offsets)
+    static constexpr int OFF_SB = SB, OFF_A = 2 * SB, OFF_B = 2 * SB + OPB;
+    static constexpr int STAGE = 2 * OPB + 2 * SB;
+    static constexpr int IPW = OPB / 1024 / NW;       // 1 KB code loads per wave per operand
+    static constexpr int SPW = 2 * SB / 256 / NW;     // 256 B scale loads per wave (both operands)
+    static constexpr int LOADS = 2 * IPW + SPW;       // vector-memory instructions per thread per stage
 };
 
-template <bool FP8>
-__device__ __forceinline__ int chunk_swz(int r) {
-    if constexpr (FP8) return (r & 7) ^ ((r >> 3) & 1);
-    return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
-}
+// 16-byte chunk slot of chunk c in row r: c ^ swz(r), distinct over any 8 consecutive rows and over
+// any 8 rows of equal parity (conflict-free 16-byte fragment reads for 32 or 64 LDS banks)
+__device__ __forceinline__ int chunk_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-__device__ __forceinline__ void wait_vm(int n) {
-    // gfx9 s_waitcnt: vmcnt in bits [3:0] and [15:14]; expcnt / lgkmcnt left at their maximum
-    switch (n) {
-        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-        case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
-        case 18: __builtin_amdgcn_s_waitcnt(0x4F72); break;
-        default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    }
+
+// s_waitcnt with vmcnt = N (gfx9 encoding: vmcnt bits [3:0] and [15:14]); expcnt and lgkmcnt at
+// their maximum, i.e. not waited for
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 template <bool FP8, bool B2D, int OUT, bool NVG>
-__global__ __launch_bounds__(256) void k_gemm_big(GemmArgs g) {
+__global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
     using C = Big<FP8>;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int wm = wave >> 2, wn = wave & 3;
 
     // tile assignment: XCD-contiguous runs, grouped by 4 tile rows
     const int ntm = (int)((g.M + C::TM - 1) / C::TM), ntn = (int)((g.N + C::TN - 1) / C::TN);
@@ -238,117 +247,152 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs g) {
 
     const int64_t rowbytes = FP8 ? g.K : g.K / 2;
     const int64_t kgroups = g.K / 32;
-    const int KT = (int)(g.K / 128);
+    const int KT = (int)(g.K / C::KSTEP);
 
-    // per-thread global source pointers for the direct-to-LDS copies (rows clamped into range:
-    // rows past M / N only feed outputs that are never stored)
-    const uint8_t* srcA[C::IPW];
-    const uint8_t* srcB[C::IPW];
+    // Direct-to-LDS copies go through buffer resources: base + 32-bit byte offset, with the K
+    // position and the row step in the scalar offset. Offsets past the end of an operand (rows
+    // beyond M or N) read as zero; those rows only feed outputs that are never stored.
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(g.M * rowbytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)g.b, (short)0, (int)(g.N * rowbytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc((void*)g.sa, (short)0, (int)(g.M * kgroups), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rSB = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)g.sb, (short)0, (int)((B2D ? (g.N + 31) / 32 : g.N) * kgroups), 0x00020000);
+    // copy i of this wave fills LDS rows r = (wave * IPW + i) * 8 + lane / 8, slot lane % 8, with
+    // chunk slot ^ swz(r) = slot ^ (lane / 8) ^ (i & 1) of the row (IPW is even)
+    const int r0 = wave * C::IPW * 8 + (lane >> 3);
+    int voA[2], voB[2];
 #pragma unroll
-    for (int i = 0; i < C::IPW; ++i) {
-        const int u = (wave * C::IPW + i) * 64 + lane;
-        const int r = u / C::CPR, slot = u % C::CPR;
-        const int c = slot ^ chunk_swz<FP8>(r);
-        const int64_t ma = (m0 + r) < g.M ? (m0 + r) : (g.M - 1);
-        const int64_t nb = (n0 + r) < g.N ? (n0 + r) : (g.N - 1);
-        srcA[i] = g.a + ma * rowbytes + 16 * c;
-        srcB[i] = g.b + nb * rowbytes + 16 * c;
+    for (int par = 0; par < 2; ++par) {
+        const int c = (lane & 7) ^ ((lane >> 3) & 7) ^ par;
+        voA[par] = (int)((m0 + r0) * rowbytes + 16 * c);
+        voB[par] = (int)((n0 + r0) * rowbytes + 16 * c);
     }
-    const int srow = wave * 64 + lane;
-    const int64_t sam = (m0 + srow) < g.M ? (m0 + srow) : (g.M - 1);
-    int64_t sbn = (n0 + srow) < g.N ? (n0 + srow) : (g.N - 1);
-    if (B2D) sbn >>= 5;
-    const uint8_t* srcSA = g.sa + sam * kgroups;
-    const uint8_t* srcSB = g.sb + sbn * kgroups;
+    // scale dwords: the stage holds SPR bytes of each of A's and B's 256 rows, row-major, as
+    // consecutive dwords; waves take them in order, A's first
+    int voS[C::SPW];
+#pragma unroll
+    for (int j = 0; j < C::SPW; ++j) {
+        const int d = (wave * C::SPW + j) * 64 + lane;       // dword index over both operands
+        const bool isb = (wave * C::SPW + j) * 64 >= C::SB / 4;
+        const int dd = isb ? d - C::SB / 4 : d;
+        const int r = dd / (C::SPR / 4), part = dd % (C::SPR / 4);
+        if (!isb) {
+            voS[j] = (int)((m0 + r) * kgroups + 4 * part);
+        } else {
+            const int64_t n = B2D ? ((n0 + r) >> 5) : (n0 + r);
+            voS[j] = (int)(n * kgroups + 4 * part);
+        }
+    }
 
     auto issue = [&](int kt) {
         uint8_t* st = smem + (kt % C::NST) * C::STAGE;
+        const int so = kt * C::RB, ss = kt * C::SPR;
 #pragma unroll
         for (int i = 0; i < C::IPW; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(srcA[i] + (int64_t)kt * C::RB),
-                                             (lds_ptr_t)(st + (wave * C::IPW + i) * 1024), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(st + C::OFF_A + (wave * C::IPW + i) * 1024), 16,
+                                                     voA[i & 1], so + (int)(8 * i * rowbytes), 0, 0);
 #pragma unroll
         for (int i = 0; i < C::IPW; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(srcB[i] + (int64_t)kt * C::RB),
-                                             (lds_ptr_t)(st + C::OPB + (wave * C::IPW + i) * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(srcSA + 4 * kt),
-                                         (lds_ptr_t)(st + 2 * C::OPB + wave * 256), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(srcSB + 4 * kt),
-                                         (lds_ptr_t)(st + 2 * C::OPB + 4 * C::TM + wave * 256), 4, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(st + C::OFF_B + (wave * C::IPW + i) * 1024),
+                                                     16, voB[i & 1], so + (int)(8 * i * rowbytes), 0, 0);
+#pragma unroll
+        for (int j = 0; j < C::SPW; ++j) {
+            if ((wave * C::SPW + j) * 64 >= C::SB / 4)  // wave-uniform
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (lds_ptr_t)(st + (wave * C::SPW + j) * 256),
+                                                         4, voS[j], ss, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_ptr_t)(st + (wave * C::SPW + j) * 256),
+                                                         4, voS[j], ss, 0, 0);
+        }
     };
 
-    v16f acc[4][4];
+    v16f acc[C::WTN][C::WTM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < C::WTN; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < C::WTM; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+    // Fragment addresses: rows of tile i of this wave are wm*128 + 32 i + l%32 (A) and
+    // wn*64 + 32 i + l%32 (B); their low 4 bits, hence the chunk swizzle, depend on the lane only,
+    // so a tile adds the constant 32 * 128 bytes and a K step only changes the chunk term.
     const int fr = lane & 31, fg = lane >> 5;
-    // loop-invariant LDS byte offsets of this lane's fragments within a stage:
-    // [kk][i][piece]; FP4 uses one 16-byte piece per fragment, FP8 two
+    const int sw = chunk_swz(fr);
     constexpr int NP = FP8 ? 2 : 1;
-    int offA[2][4][NP], offB[2][4][NP], offSA[4], offSB[4];
+    int ch[C::NKK][NP];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ra = wm * 128 + 32 * i + fr, rb = wn * 128 + 32 * i + fr;
+    for (int kk = 0; kk < C::NKK; ++kk)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                const int c = FP8 ? (4 * kk + 2 * p + fg) : (2 * kk + fg);
-                offA[kk][i][p] = ra * C::RB + 16 * (c ^ chunk_swz<FP8>(ra));
-                offB[kk][i][p] = C::OPB + rb * C::RB + 16 * (c ^ chunk_swz<FP8>(rb));
-            }
-        offSA[i] = 2 * C::OPB + 4 * ra;
-        offSB[i] = 2 * C::OPB + 4 * C::TM + 4 * rb;
-    }
+        for (int p = 0; p < NP; ++p) {
+            const int c = FP8 ? (4 * kk + 2 * p + fg) : (2 * kk + fg);
+            ch[kk][p] = 16 * (c ^ sw);
+        }
+    const int aRow = C::OFF_A + (wm * 128 + fr) * C::RB, bRow = C::OFF_B + (wn * 64 + fr) * C::RB;
+    const int aScl = C::SPR * (wm * 128 + fr), bScl = C::OFF_SB + C::SPR * (wn * 64 + fr);
     const int sshift = 8 * fg;
 
-#pragma unroll
-    for (int s = 0; s < C::NST - 1; ++s)
-        if (s < KT) issue(s);
+    issue(0);
 
-    auto compute = [&](const uint8_t* st) {
-        int sa[4], sb[4];
-        v8i fa[2][4], fb[2][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sa[i] = (int)(*reinterpret_cast<const uint32_t*>(st + offSA[i]) >> sshift);
-            sb[i] = (int)(*reinterpret_cast<const uint32_t*>(st + offSB[i]) >> sshift);
+    auto frag = [&](const uint8_t* p0, const uint8_t* p1) -> v8i {
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(p0);
+        if constexpr (!FP8) {
+            return (v8i){(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], 0, 0, 0, 0};
+        } else {
+            const u32x4 x1 = *reinterpret_cast<const u32x4*>(p1);
+            return (v8i){(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                         (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
         }
+    };
+
+    // One stage: NKK 64-deep steps. Fragments are double-buffered in registers: the reads for step
+    // kk + 1 are issued while the MFMAs of step kk run, interleaved one read per MFMA.
+    auto load_frags = [&](const uint8_t* st, int kk, v8i (&fa)[C::WTM], v8i (&fb)[C::WTN]) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int i = 0; i < C::WTM; ++i)
+            fa[i] = frag(st + aRow + 32 * C::RB * i + ch[kk][0], st + aRow + 32 * C::RB * i + ch[kk][NP - 1]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x4 xa0 = *reinterpret_cast<const u32x4*>(st + offA[kk][i][0]);
-                const u32x4 xb0 = *reinterpret_cast<const u32x4*>(st + offB[kk][i][0]);
-                if constexpr (!FP8) {
-                    fa[kk][i] = (v8i){(int)xa0[0], (int)xa0[1], (int)xa0[2], (int)xa0[3], 0, 0, 0, 0};
-                    fb[kk][i] = (v8i){(int)xb0[0], (int)xb0[1], (int)xb0[2], (int)xb0[3], 0, 0, 0, 0};
-                } else {
-                    const u32x4 xa1 = *reinterpret_cast<const u32x4*>(st + offA[kk][i][NP - 1]);
-                    const u32x4 xb1 = *reinterpret_cast<const u32x4*>(st + offB[kk][i][NP - 1]);
-                    fa[kk][i] = (v8i){(int)xa0[0], (int)xa0[1], (int)xa0[2], (int)xa0[3],
-                                      (int)xa1[0], (int)xa1[1], (int)xa1[2], (int)xa1[3]};
-                    fb[kk][i] = (v8i){(int)xb0[0], (int)xb0[1], (int)xb0[2], (int)xb0[3],
-                                      (int)xb1[0], (int)xb1[1], (int)xb1[2], (int)xb1[3]};
-                }
-            }
+        for (int i = 0; i < C::WTN; ++i)
+            fb[i] = frag(st + bRow + 32 * C::RB * i + ch[kk][0], st + bRow + 32 * C::RB * i + ch[kk][NP - 1]);
+    };
+    auto compute = [&](const uint8_t* st) {
+        int sa[C::WTM][C::SPR / 4], sb[C::WTN][C::SPR / 4];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int i = 0; i < C::WTM; ++i)
 #pragma unroll
-            for (int in = 0; in < 4; ++in)
+            for (int d = 0; d < C::SPR / 4; ++d)
+                sa[i][d] = (int)(*reinterpret_cast<const uint32_t*>(st + aScl + C::SPR * 32 * i + 4 * d) >> sshift);
 #pragma unroll
-                for (int im = 0; im < 4; ++im) {
-                    if (kk == 0)
+        for (int i = 0; i < C::WTN; ++i)
+#pragma unroll
+            for (int d = 0; d < C::SPR / 4; ++d)
+                sb[i][d] = (int)(*reinterpret_cast<const uint32_t*>(st + bScl + C::SPR * 32 * i + 4 * d) >> sshift);
+        v8i fa[2][C::WTM], fb[2][C::WTN];
+        load_frags(st, 0, fa[0], fb[0]);
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; ++kk) {
+            const int cur = kk & 1, nxt = cur ^ 1;
+            if (kk + 1 < C::NKK) load_frags(st, kk + 1, fa[nxt], fb[nxt]);
+            // scale byte of group 2 kk + (l / 32): dword kk / 2 after the lane shift, byte 2 (kk % 2)
+#pragma unroll
+            for (int in = 0; in < C::WTN; ++in)
+#pragma unroll
+                for (int im = 0; im < C::WTM; ++im) {
+                    if ((kk & 1) == 0)
                         acc[in][im] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fb[0][in], fa[0][im], acc[in][im], FP8 ? 0 : 4, FP8 ? 0 : 4, 0, sb[in], 0, sa[im]);
+                            fb[cur][in], fa[cur][im], acc[in][im], FP8 ? 0 : 4, FP8 ? 0 : 4, 0,
+                            sb[in][kk >> 1], 0, sa[im][kk >> 1]);
                     else
                         acc[in][im] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fb[1][in], fa[1][im], acc[in][im], FP8 ? 0 : 4, FP8 ? 0 : 4, 2, sb[in], 2, sa[im]);
+                            fb[cur][in], fa[cur][im], acc[in][im], FP8 ? 0 : 4, FP8 ? 0 : 4, 2,
+                            sb[in][kk >> 1], 2, sa[im][kk >> 1]);
                 }
+            // issue the next step's reads first, then this step's MFMAs; nothing moves across
+            // step boundaries
+            if (kk + 1 < C::NKK) __builtin_amdgcn_sched_group_barrier(0x100, (C::WTM + C::WTN) * NP, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, C::WTM * C::WTN, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     // main loop, unrolled by the stage count so every stage base is a constant
@@ -357,51 +401,55 @@ __global__ __launch_bounds__(256) void k_gemm_big(GemmArgs g) {
         for (int s = 0; s < C::NST; ++s) {
             const int kt = k0 + s;
             if (kt < KT) {
-                // stage kt's copies are done once at most the next stage's copies are in flight
-                if (C::NST > 2 && kt + 1 < KT) wait_vm(C::LOADS);
-                else wait_vm(0);
-                __builtin_amdgcn_s_barrier();
-                if (kt + C::NST - 1 < KT) issue(kt + C::NST - 1);
+                wait_vm<0>();                 // this wave's copies of stage kt have landed
+                __builtin_amdgcn_s_barrier();  // ... and everyone's; stage kt-1 is no longer read
+                if (kt + 1 < KT) issue(kt + 1);
                 compute(smem + s * C::STAGE);
             }
         }
     }
 
     // epilogue: lane holds, per 4-register group q, C[m][n .. n+3] with m = tile row base + l % 32,
-    // n = tile column base + 8 q + 4 (l / 32)
+    // n = tile column base + 8 q + 4 (l / 32). An opaque zero keeps the compiler from computing the
+    // output addresses before the main loop, where they would only add register pressure.
+    int opaque_zero;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(opaque_zero));
+    const int64_t me0 = m0 + opaque_zero, ne0 = n0 + opaque_zero, ldc = g.ldc + opaque_zero;
+    char* const cbase = reinterpret_cast<char*>(g.c) + opaque_zero;
+    const int64_t Mx = g.M + opaque_zero, Nx = g.N + opaque_zero;
     float gscale = 1.0f;
     if constexpr (NVG) gscale = (*g.ga) * (*g.gb);
 #pragma unroll
-    for (int im = 0; im < 4; ++im) {
-        const int64_t m = m0 + wm * 128 + 32 * im + fr;
-        if (m >= g.M) continue;
+    for (int im = 0; im < C::WTM; ++im) {
+        const int64_t m = me0 + wm * 128 + 32 * im + fr;
+        if (m >= Mx) continue;
 #pragma unroll
-        for (int in = 0; in < 4; ++in)
+        for (int in = 0; in < C::WTN; ++in)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t n = n0 + wn * 128 + 32 * in + 8 * q + 4 * fg;
+                const int64_t n = ne0 + wn * 64 + 32 * in + 8 * q + 4 * fg;
                 float v[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) v[i] = NVG ? acc[in][im][4 * q + i] * gscale : acc[in][im][4 * q + i];
                 if constexpr (OUT == DT_F32) {
-                    float* cp = reinterpret_cast<float*>(g.c) + m * g.ldc + n;
-                    if (n + 3 < g.N && ((g.ldc & 3) == 0)) {
+                    float* cp = reinterpret_cast<float*>(cbase) + m * ldc + n;
+                    if (n + 3 < Nx && ((ldc & 3) == 0)) {
                         *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
                     } else {
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            if (n + i < g.N) cp[i] = v[i];
+                            if (n + i < Nx) cp[i] = v[i];
                     }
                 } else {
-                    uint16_t* cp = reinterpret_cast<uint16_t*>(g.c) + m * g.ldc + n;
-                    if (n + 3 < g.N && ((g.ldc & 3) == 0)) {
+                    uint16_t* cp = reinterpret_cast<uint16_t*>(cbase) + m * ldc + n;
+                    if (n + 3 < Nx && ((ldc & 3) == 0)) {
                         const uint32_t w0 = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
                         const uint32_t w1 = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
                         *reinterpret_cast<uint2*>(cp) = make_uint2(w0, w1);
                     } else {
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            if (n + i < g.N) cp[i] = (uint16_t)bf16_rne_bits(v[i]);
+                            if (n + i < Nx) cp[i] = (uint16_t)bf16_rne_bits(v[i]);
                     }
                 }
             }
@@ -447,18 +495,22 @@ __global__ __launch_bounds__(256) void k_nv_to_fp8(const uint8_t* codes, const u
 
 template <bool FP8, bool B2D, bool NVG>
 static hipError_t launch_out(const GemmArgs& g, int c_dtype, hipStream_t s) {
-    if (g.M >= 256 && g.N >= 256) {
+    const int64_t rowb = FP8 ? g.K : g.K / 2;
+    if (g.M >= 256 && g.N >= 256 && g.K % Big<FP8>::KSTEP == 0 && g.M * rowb < (1ll << 31) &&
+        g.N * rowb < (1ll << 31)) {
         using C = Big<FP8>;
         const unsigned tiles = (unsigned)(((g.M + 255) / 256) * ((g.N + 255) / 256));
         const size_t lds = (size_t)C::NST * C::STAGE;
         if (c_dtype == DT_BF16) {
             auto k = k_gemm_big<FP8, B2D, DT_BF16, NVG>;
-            hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            hipLaunchKernelGGL(k, dim3(tiles), dim3(256), lds, s, g);
+            hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(k, dim3(tiles), dim3(C::NTH), lds, s, g);
         } else {
             auto k = k_gemm_big<FP8, B2D, DT_F32, NVG>;
-            hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            hipLaunchKernelGGL(k, dim3(tiles), dim3(256), lds, s, g);
+            hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(k, dim3(tiles), dim3(C::NTH), lds, s, g);
         }
         return hipGetLastError();
     }
