@@ -226,6 +226,21 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Workgroup barrier without the memory fence of __syncthreads (which waits for every outstanding
+// vector-memory operation, including the next stage's prefetch). The empty asm statements keep
+// the compiler from moving LDS or memory accesses across it; the caller waits for what must have
+// completed.
+__device__ __forceinline__ void barrier_only() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS reads and writes have completed
+__device__ __forceinline__ void wait_lgkm0() {
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+
 template <bool FP8, bool B2D, int OUT, bool NVG>
 __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
     using C = Big<FP8>;
@@ -401,58 +416,86 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
         for (int s = 0; s < C::NST; ++s) {
             const int kt = k0 + s;
             if (kt < KT) {
-                wait_vm<0>();                 // this wave's copies of stage kt have landed
-                __builtin_amdgcn_s_barrier();  // ... and everyone's; stage kt-1 is no longer read
+                wait_vm<0>();    // this wave's copies of stage kt have landed
+                barrier_only();  // ... and everyone's; stage kt-1 is no longer read
                 if (kt + 1 < KT) issue(kt + 1);
                 compute(smem + s * C::STAGE);
             }
         }
     }
 
-    // epilogue: lane holds, per 4-register group q, C[m][n .. n+3] with m = tile row base + l % 32,
-    // n = tile column base + 8 q + 4 (l / 32). An opaque zero keeps the compiler from computing the
-    // output addresses before the main loop, where they would only add register pressure.
+    // Epilogue, staged through LDS so that every global store writes whole 16-byte pieces of a
+    // row and consecutive lanes cover consecutive bytes. Lane (fr, fg) holds, for 4-register group
+    // q of tile (im, in), C[m][n .. n+3] with m = wm*128 + 32 im + fr and
+    // n = wn*64 + 32 in + 8 q + 4 fg. A pass stages 256 rows x 512 bytes: bf16 output in one pass
+    // (all 256 columns), fp32 output in two (pass p holds columns wn*64 + 32 p + [0, 32) of each
+    // wave column wn, i.e. four 128-byte runs per row).
+    constexpr int EP = 528;                       // staged row pitch (512 B + 16 B of padding)
+    static_assert(256 * EP <= C::NST * C::STAGE, "staging buffer exceeds the stage buffers");
+    constexpr int PASSES = OUT == DT_F32 ? 2 : 1;
+    float gscale = 1.0f;
+    if constexpr (NVG) gscale = (*g.ga) * (*g.gb);
+    // an opaque zero keeps the compiler from computing the output addresses before the main
+    // loop, where they would only add register pressure
     int opaque_zero;
     asm volatile("s_mov_b32 %0, 0" : "=s"(opaque_zero));
     const int64_t me0 = m0 + opaque_zero, ne0 = n0 + opaque_zero, ldc = g.ldc + opaque_zero;
     char* const cbase = reinterpret_cast<char*>(g.c) + opaque_zero;
     const int64_t Mx = g.M + opaque_zero, Nx = g.N + opaque_zero;
-    float gscale = 1.0f;
-    if constexpr (NVG) gscale = (*g.ga) * (*g.gb);
+    constexpr int ESZ = OUT == DT_F32 ? 4 : 2;
+    // 16-byte stores need a 16-byte aligned row start
+    const bool vec_ok = ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) && ((ldc * ESZ) % 16 == 0);
 #pragma unroll
-    for (int im = 0; im < C::WTM; ++im) {
-        const int64_t m = me0 + wm * 128 + 32 * im + fr;
-        if (m >= Mx) continue;
+    for (int p = 0; p < PASSES; ++p) {
+        barrier_only();  // every wave is done reading the stage buffers / the last pass
 #pragma unroll
-        for (int in = 0; in < C::WTN; ++in)
+        for (int im = 0; im < C::WTM; ++im)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t n = ne0 + wn * 64 + 32 * in + 8 * q + 4 * fg;
-                float v[4];
+            for (int inn = 0; inn < (OUT == DT_F32 ? 1 : C::WTN); ++inn) {
+                const int in = OUT == DT_F32 ? p : inn;
+                const int row = wm * 128 + 32 * im + fr;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = NVG ? acc[in][im][4 * q + i] * gscale : acc[in][im][4 * q + i];
-                if constexpr (OUT == DT_F32) {
-                    float* cp = reinterpret_cast<float*>(cbase) + m * ldc + n;
-                    if (n + 3 < Nx && ((ldc & 3) == 0)) {
-                        *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
+                for (int q = 0; q < 4; ++q) {
+                    float v[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = NVG ? acc[in][im][4 * q + i] * gscale : acc[in][im][4 * q + i];
+                    if constexpr (OUT == DT_F32) {
+                        const int col = wn * 32 + 8 * q + 4 * fg;
+                        *reinterpret_cast<f32x4*>(smem + row * EP + 4 * col) = (f32x4){v[0], v[1], v[2], v[3]};
                     } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (n + i < Nx) cp[i] = v[i];
-                    }
-                } else {
-                    uint16_t* cp = reinterpret_cast<uint16_t*>(cbase) + m * ldc + n;
-                    if (n + 3 < Nx && ((ldc & 3) == 0)) {
+                        const int col = wn * 64 + 32 * in + 8 * q + 4 * fg;
                         const uint32_t w0 = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
                         const uint32_t w1 = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
-                        *reinterpret_cast<uint2*>(cp) = make_uint2(w0, w1);
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (n + i < Nx) cp[i] = (uint16_t)bf16_rne_bits(v[i]);
+                        *reinterpret_cast<u32x2*>(smem + row * EP + 2 * col) = (u32x2){w0, w1};
                     }
                 }
             }
+        wait_lgkm0();
+        barrier_only();
+        // 32 lanes per row, 16 rows per sweep of the workgroup
+        const int c16 = tid & 31;
+        const int64_t n = OUT == DT_F32 ? ne0 + (c16 >> 3) * 64 + 32 * p + 4 * (c16 & 7) : ne0 + 8 * c16;
+        constexpr int EPC = 16 / ESZ;  // elements per 16-byte piece
+#pragma unroll 4
+        for (int r = tid >> 5; r < 256; r += C::NTH / 32) {
+            const int64_t m = me0 + r;
+            if (m >= Mx) break;
+            const u32x4 val = *reinterpret_cast<const u32x4*>(smem + r * EP + 16 * c16);
+            char* cp = cbase + (m * ldc + n) * ESZ;
+            if (vec_ok && n + EPC <= Nx) {
+                *reinterpret_cast<u32x4*>(cp) = val;
+            } else {
+#pragma unroll
+                for (int i = 0; i < EPC; ++i) {
+                    if (n + i < Nx) {
+                        if constexpr (OUT == DT_F32)
+                            reinterpret_cast<uint32_t*>(cp)[i] = val[i];
+                        else
+                            reinterpret_cast<uint16_t*>(cp)[i] = (uint16_t)(val[i >> 1] >> (16 * (i & 1)));
+                    }
+                }
+            }
+        }
     }
 }
 
