@@ -24,27 +24,82 @@ namespace bgf {
 
 constexpr int kThreads = 256;
 
+// 16-byte pieces per 32-element segment, and the LDS slice a wave needs to transpose 64 of them
 template <int IN>
-__device__ __forceinline__ void load_segment(const void* base, float (&v)[32]) {
-    if constexpr (IN == DT_BF16) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(base);
+struct SegIO {
+    static constexpr int P = IN == DT_BF16 ? 4 : 8;
+    static constexpr int ESZ = IN == DT_BF16 ? 2 : 4;
+};
+
+// Gives every lane of the wave the 32 elements of segment `lane` of a 64-segment wave tile.
+// Piece ch = 64 i + lane (16 bytes: piece ch % P of tile segment ch / P) is read from byte offset
+// off[i] of the buffer rs (offsets past the buffer's extent, such as -1, read as zeros). The loads
+// are wave-wide and 16 bytes per lane, consecutive lanes reading consecutive pieces (whole cache
+// lines wherever segments are adjacent in memory); the pieces are then transposed through the
+// wave's own LDS slice, piece q of segment s at 16-byte slot P s + (q ^ ((s / G) % P)) with
+// G = 16 / P, so that both the writes and the reads of any 16 consecutive lanes touch 16 distinct
+// slots of one 256-byte bank sweep. A wave's LDS accesses complete in order, so the read-back needs
+// no barrier.
+template <int IN>
+__device__ __forceinline__ void load_wave_segments(__amdgpu_buffer_rsrc_t rs, const int (&off)[SegIO<IN>::P],
+                                                   u32x4* lds, float (&v)[32]) {
+    constexpr int P = SegIO<IN>::P, G = 16 / P;
+    const int lane = __lane_id();
+    u32x4 raw[P];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x4 w = __builtin_nontemporal_load(p + i);
+    for (int i = 0; i < P; ++i) raw[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, 2 /* nt */);
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int ch = 64 * i + lane, sg = ch / P, q = ch % P;
+        lds[P * sg + (q ^ ((sg / G) % P))] = raw[i];
+    }
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const u32x4 w = lds[P * lane + (q ^ ((lane / G) % P))];
+        if constexpr (IN == DT_BF16) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                v[8 * i + 2 * j] = bf16_lo(w[j]);
-                v[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+                v[8 * q + 2 * j] = bf16_lo(w[j]);
+                v[8 * q + 2 * j + 1] = bf16_hi(w[j]);
             }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[4 * q + j] = __uint_as_float(w[j]);
         }
+    }
+}
+
+// Loads the wave tile of 64 consecutive segments wbase .. wbase + 63 of a row-major [rows, cols]
+// tensor with row pitch ldx (segments past nseg read as zeros).
+template <int IN>
+__device__ __forceinline__ void load_wave_segments_1d(const SegArgs& a, int64_t wbase, u32x4* lds, float (&v)[32]) {
+    constexpr int P = SegIO<IN>::P, ESZ = SegIO<IN>::ESZ;
+    const int lane = __lane_id();
+    const int64_t spr = a.cols >> 5;
+    const char* const xb = reinterpret_cast<const char*>(a.x);
+    int off[P];
+    if (a.ldx == a.cols) {
+        // contiguous rows: the tile is one run of bytes; the extent stops at the tensor's end
+        const int64_t left = (a.nseg - wbase) * 32 * ESZ;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(xb + wbase * 32 * ESZ), (short)0, (int)(left < 64 * 32 * ESZ ? left : 64 * 32 * ESZ), 0x00020000);
+#pragma unroll
+        for (int i = 0; i < P; ++i) off[i] = 16 * (64 * i + lane);
+        load_wave_segments<IN>(rs, off, lds, v);
     } else {
-        const f32x4* p = reinterpret_cast<const f32x4*>(base);
+        // strided rows: per-piece offsets from the tile's first segment (row pitch below 32 MiB)
+        const int64_t r0 = wbase / spr;
+        const int64_t base = r0 * a.ldx + (wbase - r0 * spr) * 32;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const f32x4 w = __builtin_nontemporal_load(p + i);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[4 * i + j] = w[j];
+        for (int i = 0; i < P; ++i) {
+            const int ch = 64 * i + lane;
+            const int64_t sg = wbase + ch / P;
+            const int64_t r = sg / spr;
+            off[i] = sg < a.nseg ? (int)((r * a.ldx + (sg - r * spr) * 32 - base) * ESZ + 16 * (ch % P)) : -1;
         }
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(xb + base * ESZ), (short)0, 0x7FFFFFFF, 0x00020000);
+        load_wave_segments<IN>(rs, off, lds, v);
     }
 }
 
@@ -257,54 +312,79 @@ __device__ __forceinline__ float f32_block(float (&v)[32], float amax, const uin
 // ---------------------------------------------------------------------------------------------
 template <int IN, int HN, int ELEM, int SC, int RND, int BR, int BC, int PASS>
 __global__ __launch_bounds__(kThreads) void k_segment(SegArgs a) {
+    constexpr int P = SegIO<IN>::P, ESZ = SegIO<IN>::ESZ;
+    __shared__ u32x4 stage[kThreads / 64][64 * P];
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;  // wave-uniform wv
     const int64_t spr = a.cols >> 5;  // segments per row
-    int64_t row, sc;
-    bool valid;
-    if constexpr (BR == 1) {
-        const int64_t seg = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-        valid = seg < a.nseg;
-        row = valid ? seg / spr : 0;
-        sc = valid ? seg - row * spr : 0;
-    } else {
-        const int64_t ngc = (spr + 7) >> 3;
-        const int64_t R = blockIdx.x / ngc, C = blockIdx.x - (blockIdx.x / ngc) * ngc;
-        row = R * 32 + (threadIdx.x >> 3);
-        sc = C * 8 + (threadIdx.x & 7);
-        valid = sc < spr;
-    }
-    const int64_t seg = row * spr + sc;
-    const int64_t c0 = sc * 32;
 
-    float v[32];
-    if (valid) {
-        const char* base = reinterpret_cast<const char*>(a.x) +
-                           (row * a.ldx + c0) * (IN == DT_BF16 ? 2 : 4);
-        load_segment<IN>(base, v);
-    } else {
+    if constexpr (PASS == PASS_AMAX) {
+        // tensor amax of the (rotated) input: a grid-stride walk over 256-segment groups, one
+        // atomic max per workgroup (non-negative floats order like their bit patterns)
+        float m = 0.0f;
+        for (int64_t g0 = (int64_t)blockIdx.x * kThreads; g0 < a.nseg; g0 += (int64_t)gridDim.x * kThreads) {
+            float v[32];
+            load_wave_segments_1d<IN>(a, g0 + 64 * wv, stage[wv], v);
+            fwht_segment<HN>(v);
+            m = fmaxf(m, block_amax<32, 0>(v));
+        }
 #pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        __shared__ float red[kThreads / 64];
+        if (lane == 0) red[wv] = m;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float t = red[0];
+#pragma unroll
+            for (int i = 1; i < kThreads / 64; ++i) t = fmaxf(t, red[i]);
+            atomicMax(a.ws, __float_as_uint(t));
+        }
+        return;
+    }
+
+    // this lane's segment: lane of a 64-segment wave tile. seg = row * spr + sc indexes codes and
+    // scales; 32 seg is the row-major index of the segment's first element.
+    int64_t seg, row = 0, sc = 0;
+    bool valid;
+    float v[32];
+    if constexpr (BR == 1) {
+        const int64_t wbase = (int64_t)blockIdx.x * kThreads + 64 * wv;
+        seg = wbase + lane;
+        valid = seg < a.nseg;
+        load_wave_segments_1d<IN>(a, wbase, stage[wv], v);
+    } else {
+        // 2D: a workgroup covers 32 rows x 8 segments, wave wv rows 8 wv .. 8 wv + 7
+        const int64_t ngc = (spr + 7) >> 3;
+        const int64_t R = blockIdx.x / (uint32_t)ngc, C = blockIdx.x - R * ngc;
+        row = R * 32 + 8 * wv + (lane >> 3);
+        sc = C * 8 + (lane & 7);
+        valid = sc < spr;
+        // wave tile: rows 8 wv + s / 8 and segment columns C * 8 + s % 8 of the workgroup's rows
+        int off[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int ch = 64 * i + lane, s2 = ch / P;
+            const int64_t c2 = C * 8 + (s2 & 7);
+            off[i] = c2 < spr ? (int)(((s2 >> 3) * a.ldx + c2 * 32) * ESZ + 16 * (ch % P)) : -1;
+        }
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(reinterpret_cast<const char*>(a.x) + (R * 32 + 8 * wv) * a.ldx * ESZ), (short)0, 0x7FFFFFFF, 0x00020000);
+        load_wave_segments<IN>(rs, off, stage[wv], v);
+        seg = row * spr + sc;
     }
     fwht_segment<HN>(v);
 
     if constexpr (PASS == PASS_ROTATE) {
         if (valid) {
-            float4* y = reinterpret_cast<float4*>(a.yrot + row * a.cols + c0);
+            float4* y = reinterpret_cast<float4*>(a.yrot + seg * 32);
 #pragma unroll
             for (int i = 0; i < 8; ++i) y[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
         }
         return;
     }
-    if constexpr (PASS == PASS_AMAX) {
-        float m = block_amax<32, 0>(v);
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-        if (__lane_id() == 0) atomicMax(a.ws, __float_as_uint(m));
-        return;
-    }
     if constexpr (PASS == PASS_QUANT) {
         uint32_t rw[16];
         if constexpr (RND == RND_SR) {
-            philox_segment(a.seed, (uint64_t)(row * a.cols + c0), rw);
+            philox_segment(a.seed, (uint64_t)seg * 32u, rw);
         }
         uint32_t out[8];
         if constexpr (BR == 32) {
@@ -599,7 +679,8 @@ static hipError_t launch_seg_q(const SegArgs& a, int pass, hipStream_t stream) {
     int64_t grid;
     if (BR == 1) grid = (a.nseg + kThreads - 1) / kThreads;
     else grid = (a.rows / 32) * (((a.cols >> 5) + 7) >> 3);
-    if (pass == PASS_AMAX) BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, 32, PASS_AMAX>), grid, a);
+    // the amax pass walks the tensor with at most 1024 workgroups (one atomic each)
+    if (pass == PASS_AMAX) BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, 32, PASS_AMAX>), (grid < 1024 ? grid : 1024), a);
     if (pass == PASS_ROTATE) BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, 32, PASS_ROTATE>), grid, a);
     BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, BR, BC, PASS_QUANT>), grid, a);
 }
