@@ -10,13 +10,22 @@ Inputs are resident in HBM before timing starts; the step cycles over several co
 
 Prints one JSON line. `value` is the step's effective throughput in TFLOP/s (GEMM FLOPs over the
 whole step time, quantization included); the per-kernel GB/s / TFLOP/s and roofline fractions are
-in the extra fields. `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
+in the extra fields. `roofline` is the dominant kernel (the GEMM): algorithmic FLOPs per launch over
+its average launch time from HIP events on the launch stream; its `traffic` is the measured memory
+traffic per launch from the committed counter summary, reported only while the summary's kernel
+source hash matches the current source. `cpu_baseline` times the CPU oracle on a bounded sample of
+the same step.
+
+`--copy-calibration MIB` instead runs only a plain device-to-device copy of MIB MiB a few times
+(the reference kernel whose FETCH_SIZE / WRITE_SIZE counter readings calibrate the GEMM's).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -26,6 +35,9 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 FP4_PEAK_TFLOPS = 10100.0       # MI355X dense MXFP4 matrix throughput, TFLOP/s
 M, N, K = 4096, 11008, 4096
 HN = 128
+ROOT = os.path.dirname(os.path.abspath(__file__))
+GEMM_SRC = os.path.join(ROOT, "bit_gemm_fwht_amd", "csrc", "gemm.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_llama7b_forward_linear_traffic.md")
 
 
 def parse():
@@ -37,7 +49,35 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-fraction", type=float, default=0.25,
                     help="fraction f of X rows and W rows the CPU oracle processes")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
+
+
+def measured_traffic():
+    """Bytes per GEMM launch from the committed counter summary, or None when it is missing or was
+    taken on another version of the kernel source."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        src = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m_src = re.search(r"kernel source sha256: ([0-9a-f]{64})", text)
+    m_b = re.search(r"calibrated bytes per launch: ([0-9]+)", text)
+    if not m_src or not m_b or m_src.group(1) != src:
+        return None
+    return int(m_b.group(1))
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib << 20
+    x = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
 def cpu_baseline(x_bits, w_bits, f):
@@ -72,8 +112,11 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
-              "rows of X / W with no exchange, see DESIGN.md", file=sys.stderr)
+              "rows of X / W with no exchange between GPUs", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
 
     from bit_gemm_fwht_amd import fp4
@@ -143,7 +186,8 @@ def main():
                    "input_copies": args.copies},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": FP4_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "k_gemm (MXFP4, 16x16x128 scaled MFMA)"},
+                     "traffic": measured_traffic(),
+                     "kernel": "k_gemm_big (MXFP4, 256x256 tiles, 32x32x64 scaled MFMA, bf16 out)"},
         "quantize_x": {"GB/s": round(bytes_x / tq_x / 1e9, 1),
                        "frac": round(bytes_x / tq_x / 1e9 / HBM_PEAK_GBS, 4),
                        "us": round(tq_x * 1e6, 2), "bytes": int(bytes_x)},
