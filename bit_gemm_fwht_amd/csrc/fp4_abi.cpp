@@ -296,11 +296,29 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
         int b2d;
         const int kind = gemm_kind(A, B, &b2d);
         if (kind < 0) return FP4_ERR_UNSUPPORTED;
-        if (out_q || C_q) return FP4_ERR_UNSUPPORTED;  // fused output quantization: not built yet
-        if (!C) return FP4_ERR_INVALID_ARG;
-        if (c_dtype != FP4_DT_F32 && c_dtype != FP4_DT_BF16) return FP4_ERR_INVALID_ARG;
-        if (ldc < N) return FP4_ERR_INVALID_ARG;
-        if (!aligned(C, 16)) return FP4_ERR_ALIGNMENT;
+        // fused output quantization: MX groups of 32 along N, E8M0 floor / ceil, no rotation
+        const bool fq = out_q != nullptr;
+        if (fq != (C_q != nullptr)) return FP4_ERR_INVALID_ARG;
+        if (fq) {
+            if (out_q->elem != FP4_ELEM_E2M1 && out_q->elem != FP4_ELEM_E4M3) return FP4_ERR_INVALID_ARG;
+            if (out_q->round_mode != FP4_ROUND_RNE && out_q->round_mode != FP4_ROUND_SR) return FP4_ERR_INVALID_ARG;
+            if (out_q->block_rows != 1 || out_q->block_cols != 32) return FP4_ERR_UNSUPPORTED;
+            if (out_q->scale_mode != FP4_SCALE_E8M0_FLOOR && out_q->scale_mode != FP4_SCALE_E8M0_CEIL)
+                return FP4_ERR_UNSUPPORTED;
+            if (out_q->hadamard_n != 0) return FP4_ERR_UNSUPPORTED;
+            if (N % 32) return FP4_ERR_INVALID_ARG;
+            if (!C_q->codes || !C_q->scales) return FP4_ERR_INVALID_ARG;
+            if (!aligned(C_q->codes, 16)) return FP4_ERR_ALIGNMENT;
+        }
+        if (!fq && !C) return FP4_ERR_INVALID_ARG;
+        if (C) {
+            if (c_dtype != FP4_DT_F32 && c_dtype != FP4_DT_BF16) return FP4_ERR_INVALID_ARG;
+            if (ldc < N) return FP4_ERR_INVALID_ARG;
+            if (!aligned(C, 16)) return FP4_ERR_ALIGNMENT;
+        } else {
+            c_dtype = FP4_DT_F32;  // selects the kernel variant only; nothing is stored
+            ldc = N;
+        }
         const int64_t need = gemm_ws(A, B, kind);
         if (need && (!workspace || ws_bytes < need)) return FP4_ERR_WORKSPACE;
         if (need && !aligned(workspace, 256)) return FP4_ERR_ALIGNMENT;
@@ -318,6 +336,19 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
         g.c = C;
         g.ldc = ldc;
         g.b_2d = b2d;
+        if (fq) {
+            g.qcodes = reinterpret_cast<uint8_t*>(C_q->codes);
+            g.qscales = reinterpret_cast<uint8_t*>(C_q->scales);
+            g.q_elem = out_q->elem == FP4_ELEM_E2M1 ? ELEM_E2M1 : ELEM_E4M3;
+            g.q_ceil = out_q->scale_mode == FP4_SCALE_E8M0_CEIL;
+            g.q_round = out_q->round_mode == FP4_ROUND_SR ? RND_SR : RND_RNE;
+            g.q_seed = out_q->seed;
+            // describe what was written
+            C_q->rows = M;
+            C_q->cols = N;
+            C_q->tensor_scale = nullptr;
+            C_q->p = *out_q;
+        }
         if (kind == 2) {
             auto r = [](int64_t x) { return (x + 255) / 256 * 256; };
             uint8_t* w = reinterpret_cast<uint8_t*>(workspace);
@@ -329,7 +360,7 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
             w += r(N * K);
             g.sb8 = w;
         }
-        return hip_status(launch_gemm(g, kind, c_dtype, 0, reinterpret_cast<hipStream_t>(stream)));
+        return hip_status(launch_gemm(g, kind, c_dtype, fq ? 1 : 0, reinterpret_cast<hipStream_t>(stream)));
     } catch (...) {
         return FP4_ERR_INTERNAL;
     }

@@ -41,7 +41,57 @@ struct Cfg {
     static constexpr int LOADS = BM * CH / NT;     // 16-byte loads per thread per operand
 };
 
-template <bool FP8, bool B2D, int OUT, bool NVG>
+// ---------------------------------------------------------------------------------------------
+// Fused output quantization ("online quantization" of the GEMM output in the QuTLASS kernel list of
+// the Quartet lecture notes): C, as the fp32 values the plain output path would store (accumulator
+// times the NVFP4 tensor-scale product), quantized along N in MX groups of 32 with the rules of the
+// quantize kernels: E8M0 floor or ceil scale from the group amax, E2M1 or E4M3 elements, round to
+// nearest even (hardware convert) or stochastic rounding keyed by the row-major index m * N + n of
+// C. Codes are [M, N/2] (E2M1) or [M, N] (E4M3) bytes, scales [M, N/32].
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ int outq_exp(const GemmArgs& g, float amax) {
+    return g.q_elem == ELEM_E2M1 ? e8m0_exp<2, 0x400000u>(amax, g.q_ceil != 0)
+                                 : e8m0_exp<8, 0x600000u>(amax, g.q_ceil != 0);
+}
+
+// Codes of v[i] = C[m][n0 + i], i = 0..3 (n0 % 4 == 0), under the scale 2^k; idx0 = m * N + n0.
+// E2M1: element i in nibble i of the low 16 bits; E4M3: element i in byte i.
+__device__ __forceinline__ uint32_t outq_encode4(const GemmArgs& g, float (&v)[4], int k, int64_t idx0) {
+    if (k == -127) {
+        // 2^-127 is not a normal fp32: divide by 2^-126 after doubling (exact for such tiny values)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = v[i] * 2.0f;
+        k = -126;
+    }
+    const float scale = pow2f(k);
+    if (g.q_round == RND_RNE) {
+        if (g.q_elem == ELEM_E2M1) {
+            uint32_t r = cvt_fp4x2<0>(0u, v[0], v[1], scale);
+            return cvt_fp4x2<1>(r, v[2], v[3], scale);
+        }
+        const float cl = 448.0f * scale;  // saturate before the non-saturating convert
+        uint32_t r = cvt_fp8x2<false>(0u, __builtin_amdgcn_fmed3f(v[0], -cl, cl), __builtin_amdgcn_fmed3f(v[1], -cl, cl), scale);
+        return cvt_fp8x2<true>(r, __builtin_amdgcn_fmed3f(v[2], -cl, cl), __builtin_amdgcn_fmed3f(v[3], -cl, cl), scale);
+    }
+    // SR: one Philox call covers elements 8 (idx0 / 8) .. + 7; element j of it takes half j % 2 of
+    // word j / 2
+    const float rcp = __builtin_amdgcn_ldexpf(1.0f, -k);
+    const uint64_t ctr = (uint64_t)idx0 >> 3;
+    uint32_t c0 = (uint32_t)ctr, c1 = (uint32_t)(ctr >> 32), c2 = 0u, c3 = 0u;
+    philox4x32_10(c0, c1, c2, c3, (uint32_t)g.q_seed, (uint32_t)(g.q_seed >> 32));
+    const bool hi = (idx0 & 7) != 0;  // elements 4..7 of the call: words 2 and 3
+    const uint32_t wa = hi ? c2 : c0, wb = hi ? c3 : c1;
+    const uint32_t u[4] = {wa & 0xFFFFu, wa >> 16, wb & 0xFFFFu, wb >> 16};
+    uint32_t r = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float x = v[i] * rcp;
+        r |= g.q_elem == ELEM_E2M1 ? e2m1_sr(x, u[i]) << (4 * i) : e4m3_sr(x, u[i]) << (8 * i);
+    }
+    return r;
+}
+
+template <bool FP8, bool B2D, int OUT, bool NVG, bool FQ>
 __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
     using C = Cfg<FP8>;
     __shared__ __attribute__((aligned(16))) uint8_t sA[BM * C::LD];
@@ -140,6 +190,43 @@ __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
     // epilogue: lane holds C[m][n .. n+3]
     float gscale = 1.0f;
     if constexpr (NVG) gscale = (*g.ga) * (*g.gb);
+    if constexpr (FQ) {
+        // a 32-column group of row m is tiles in = 2 gq, 2 gq + 1 of lanes fr, fr + 16, fr + 32,
+        // fr + 48: 8 values per lane, amax over the four lanes
+#pragma unroll
+        for (int im = 0; im < 4; ++im)
+#pragma unroll
+            for (int gq = 0; gq < 2; ++gq) {
+                const int64_t m = m0 + wm * 64 + 16 * im + fr;
+                const int64_t nb = n0 + wn * 64 + 32 * gq;
+                float v0[4], v1[4];
+                float amax = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v0[i] = NVG ? acc[2 * gq][im][i] * gscale : acc[2 * gq][im][i];
+                    v1[i] = NVG ? acc[2 * gq + 1][im][i] * gscale : acc[2 * gq + 1][im][i];
+                    amax = fmaxf(amax, fmaxf(fabsf(v0[i]), fabsf(v1[i])));
+                }
+                amax = fmaxf(amax, __shfl_xor(amax, 16));
+                amax = fmaxf(amax, __shfl_xor(amax, 32));
+                const int k = outq_exp(g, amax);
+                const uint32_t p0 = outq_encode4(g, v0, k, m * g.N + nb + 4 * fg);
+                const uint32_t p1 = outq_encode4(g, v1, k, m * g.N + nb + 16 + 4 * fg);
+                if (m < g.M && nb < g.N) {
+                    if (g.q_elem == ELEM_E2M1) {
+                        uint8_t* q = g.qcodes + m * (g.N / 2) + nb / 2;
+                        *reinterpret_cast<uint16_t*>(q + 2 * fg) = (uint16_t)p0;
+                        *reinterpret_cast<uint16_t*>(q + 8 + 2 * fg) = (uint16_t)p1;
+                    } else {
+                        uint8_t* q = g.qcodes + m * g.N + nb;
+                        *reinterpret_cast<uint32_t*>(q + 4 * fg) = p0;
+                        *reinterpret_cast<uint32_t*>(q + 16 + 4 * fg) = p1;
+                    }
+                    if (fg == 0) g.qscales[m * (g.N / 32) + nb / 32] = (uint8_t)(k + 127);
+                }
+            }
+        if (!g.c) return;
+    }
 #pragma unroll
     for (int in = 0; in < 4; ++in)
 #pragma unroll
@@ -241,7 +328,7 @@ __device__ __forceinline__ void wait_lgkm0() {
     __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
 }
 
-template <bool FP8, bool B2D, int OUT, bool NVG>
+template <bool FP8, bool B2D, int OUT, bool NVG, bool FQ>
 __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
     using C = Big<FP8>;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -442,6 +529,49 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
     const int64_t me0 = m0 + opaque_zero, ne0 = n0 + opaque_zero, ldc = g.ldc + opaque_zero;
     char* const cbase = reinterpret_cast<char*>(g.c) + opaque_zero;
     const int64_t Mx = g.M + opaque_zero, Nx = g.N + opaque_zero;
+    if constexpr (FQ) {
+        // fused output quantization: tile (im, in) of this wave is one 32-column group of each of
+        // its 32 rows; lane (fr, fg) holds 16 of the group's values (columns 8 q + 4 fg + i), lane
+        // fr + 32 (1 - fg) the other 16
+#pragma unroll
+        for (int im = 0; im < C::WTM; ++im)
+#pragma unroll
+            for (int in = 0; in < C::WTN; ++in) {
+                const int64_t m = me0 + wm * 128 + 32 * im + fr;
+                const int64_t nb = ne0 + wn * 64 + 32 * in;
+                float v[4][4];
+                float amax = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v[q][i] = NVG ? acc[in][im][4 * q + i] * gscale : acc[in][im][4 * q + i];
+                        amax = fmaxf(amax, fabsf(v[q][i]));
+                    }
+                amax = fmaxf(amax, __shfl_xor(amax, 32));
+                const int k = outq_exp(g, amax);
+                uint32_t part[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) part[q] = outq_encode4(g, v[q], k, m * Nx + nb + 8 * q + 4 * fg);
+                // swap halves with the partner lane so that each lane holds one contiguous half of
+                // the group's codes: lane fg = 0 the first, fg = 1 the second
+                if (g.q_elem == ELEM_E2M1) {
+                    const uint32_t send = fg ? (part[0] | (part[1] << 16)) : (part[2] | (part[3] << 16));
+                    const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
+                    const uint32_t d0 = fg ? ((recv & 0xFFFFu) | (part[2] << 16)) : (part[0] | (recv << 16));
+                    const uint32_t d1 = fg ? ((recv >> 16) | (part[3] << 16)) : (part[1] | (recv & 0xFFFF0000u));
+                    if (m < Mx && nb < Nx)
+                        *reinterpret_cast<u32x2*>(g.qcodes + m * (Nx / 2) + nb / 2 + 8 * fg) = (u32x2){d0, d1};
+                } else {
+                    const uint32_t r0 = (uint32_t)__shfl_xor((int)(fg ? part[0] : part[2]), 32);
+                    const uint32_t r1 = (uint32_t)__shfl_xor((int)(fg ? part[1] : part[3]), 32);
+                    const u32x4 d = fg ? (u32x4){r0, part[2], r1, part[3]} : (u32x4){part[0], r0, part[1], r1};
+                    if (m < Mx && nb < Nx) *reinterpret_cast<u32x4*>(g.qcodes + m * Nx + nb + 16 * fg) = d;
+                }
+                if (fg == 0 && m < Mx && nb < Nx) g.qscales[m * (Nx / 32) + nb / 32] = (uint8_t)(k + 127);
+            }
+        if (!g.c) return;
+    }
     constexpr int ESZ = OUT == DT_F32 ? 4 : 2;
     // 16-byte stores need a 16-byte aligned row start
     const bool vec_ok = ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) && ((ldc * ESZ) % 16 == 0);
@@ -536,7 +666,7 @@ __global__ __launch_bounds__(256) void k_nv_to_fp8(const uint8_t* codes, const u
     dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-template <bool FP8, bool B2D, bool NVG>
+template <bool FP8, bool B2D, bool NVG, bool FQ>
 static hipError_t launch_out(const GemmArgs& g, int c_dtype, hipStream_t s) {
     const int64_t rowb = FP8 ? g.K : g.K / 2;
     if (g.M >= 256 && g.N >= 256 && g.K % Big<FP8>::KSTEP == 0 && g.M * rowb < (1ll << 31) &&
@@ -545,12 +675,12 @@ static hipError_t launch_out(const GemmArgs& g, int c_dtype, hipStream_t s) {
         const unsigned tiles = (unsigned)(((g.M + 255) / 256) * ((g.N + 255) / 256));
         const size_t lds = (size_t)C::NST * C::STAGE;
         if (c_dtype == DT_BF16) {
-            auto k = k_gemm_big<FP8, B2D, DT_BF16, NVG>;
+            auto k = k_gemm_big<FP8, B2D, DT_BF16, NVG, FQ>;
             hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
             hipLaunchKernelGGL(k, dim3(tiles), dim3(C::NTH), lds, s, g);
         } else {
-            auto k = k_gemm_big<FP8, B2D, DT_F32, NVG>;
+            auto k = k_gemm_big<FP8, B2D, DT_F32, NVG, FQ>;
             hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
             hipLaunchKernelGGL(k, dim3(tiles), dim3(C::NTH), lds, s, g);
@@ -558,18 +688,18 @@ static hipError_t launch_out(const GemmArgs& g, int c_dtype, hipStream_t s) {
         return hipGetLastError();
     }
     dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM));
-    if (c_dtype == DT_BF16) hipLaunchKernelGGL((k_gemm<FP8, B2D, DT_BF16, NVG>), grid, dim3(NT), 0, s, g);
-    else hipLaunchKernelGGL((k_gemm<FP8, B2D, DT_F32, NVG>), grid, dim3(NT), 0, s, g);
+    if (c_dtype == DT_BF16) hipLaunchKernelGGL((k_gemm<FP8, B2D, DT_BF16, NVG, FQ>), grid, dim3(NT), 0, s, g);
+    else hipLaunchKernelGGL((k_gemm<FP8, B2D, DT_F32, NVG, FQ>), grid, dim3(NT), 0, s, g);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmArgs& g, int kind, int c_dtype, int fused_q, hipStream_t s) {
-    (void)fused_q;
+template <bool FQ>
+static hipError_t launch_kind(const GemmArgs& g, int kind, int c_dtype, hipStream_t s) {
     if (kind == 0) {
-        if (g.b_2d) return launch_out<false, true, false>(g, c_dtype, s);
-        return launch_out<false, false, false>(g, c_dtype, s);
+        if (g.b_2d) return launch_out<false, true, false, FQ>(g, c_dtype, s);
+        return launch_out<false, false, false, FQ>(g, c_dtype, s);
     }
-    if (kind == 1) return launch_out<true, false, false>(g, c_dtype, s);
+    if (kind == 1) return launch_out<true, false, false, FQ>(g, c_dtype, s);
     // NVFP4: re-express both operands, then the FP8 product with the tensor scales
     const int64_t ga = g.M * (g.K / 32), gb = g.N * (g.K / 32);
     hipLaunchKernelGGL(k_nv_to_fp8, dim3((unsigned)((ga + 255) / 256)), dim3(256), 0, s, g.a, g.sa, g.M, g.K, g.a8, g.sa8);
@@ -583,7 +713,12 @@ hipError_t launch_gemm(const GemmArgs& g, int kind, int c_dtype, int fused_q, hi
     h.b = g.b8;
     h.sa = g.sa8;
     h.sb = g.sb8;
-    return launch_out<true, false, true>(h, c_dtype, s);
+    return launch_out<true, false, true, FQ>(h, c_dtype, s);
+}
+
+hipError_t launch_gemm(const GemmArgs& g, int kind, int c_dtype, int fused_q, hipStream_t s) {
+    if (fused_q) return launch_kind<true>(g, kind, c_dtype, s);
+    return launch_kind<false>(g, kind, c_dtype, s);
 }
 
 }  // namespace bgf

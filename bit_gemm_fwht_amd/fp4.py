@@ -204,19 +204,35 @@ def gemm_workspace_bytes(a: QTensor, b: QTensor) -> int:
 
 
 def gemm(a: QTensor, b: QTensor, out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
-         workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """C [M, N] = A [M, K] * B [N, K]^T on quantized operands (fp32 accumulation)."""
+         workspace: torch.Tensor | None = None, out_q: Params | None = None,
+         q_out: QTensor | None = None, keep_c: bool = True):
+    """C [M, N] = A [M, K] * B [N, K]^T on quantized operands (fp32 accumulation).
+
+    With out_q (MX groups of 32 along N, E8M0 floor / ceil, RNE or SR), C is also quantized in the
+    epilogue and (C, C_q) is returned; keep_c=False skips writing C and returns (None, C_q)."""
     dev = a.codes.device
-    c = out if out is not None else torch.empty(a.rows, b.rows, dtype=out_dtype, device=dev)
+    c = None
+    if out_q is None or keep_c:
+        c = out if out is not None else torch.empty(a.rows, b.rows, dtype=out_dtype, device=dev)
     wb = gemm_workspace_bytes(a, b)
     if wb and workspace is None:
         workspace = torch.empty(wb, dtype=torch.uint8, device=dev)
     ac, bc = a.c(), b.c()
-    st = lib().fp4_gemm(ctypes.byref(ac), ctypes.byref(bc), c.data_ptr(), _dtype_code(c),
-                        c.stride(0), None, None,
+    qp = qc = None
+    if out_q is not None:
+        if q_out is None:
+            q_out = empty_qtensor(a.rows, b.rows, out_q, dev)
+        qp = out_q.c()
+        qc = q_out.c()
+    st = lib().fp4_gemm(ctypes.byref(ac), ctypes.byref(bc), c.data_ptr() if c is not None else None,
+                        _dtype_code(c) if c is not None else 0, c.stride(0) if c is not None else 0,
+                        ctypes.byref(qp) if qp is not None else None,
+                        ctypes.byref(qc) if qc is not None else None,
                         workspace.data_ptr() if workspace is not None else None,
                         workspace.numel() if workspace is not None else 0, _stream_ptr(dev))
     _check(st, "fp4_gemm")
+    if out_q is not None:
+        return c, q_out
     return c
 
 

@@ -149,9 +149,14 @@ int fp4_hadamard(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int
  * cores, and the product of the two tensor scales is applied in the epilogue).
  * K % 128 == 0. Operands must not be rotated differently: a rotation along K cancels in A B^T
  * only when both were rotated with the same n, which the caller ensures.
- * Optional fused output quantization: if out_q is non-NULL, C_q receives the fp32 result
- * quantized along N with *out_q (E2M1 or E4M3 elements, E8M0 floor/ceil, (1, 32) groups, RNE or
- * SR, no rotation); C may then be NULL. workspace: fp4_gemm_workspace_bytes() bytes. */
+ * Optional fused output quantization ("online quantization" of the output in the QuTLASS kernel
+ * list of the Quartet notes): if out_q is non-NULL, C_q->codes / C_q->scales (device, codes
+ * 16-byte aligned) receive the fp32 result -- the value an fp32 C would hold -- quantized along N
+ * exactly as fp4_quantize would quantize that fp32 C with *out_q: E2M1 or E4M3 elements, E8M0
+ * floor or ceil scales, (1, 32) groups, RNE or SR (element (m, n) keyed by m * N + n), no
+ * rotation. Requires N % 32 == 0; C_q->rows, cols, p are set to M, N, *out_q and tensor_scale to
+ * NULL. C may then be NULL (only the quantized output is written); out_q and C_q are given
+ * together or not at all. workspace: fp4_gemm_workspace_bytes() bytes. */
 int64_t fp4_gemm_workspace_bytes(const fp4_qtensor* A, const fp4_qtensor* B);
 int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtype, int64_t ldc,
              const fp4_qparams* out_q, fp4_qtensor* C_q, void* workspace, int64_t ws_bytes,

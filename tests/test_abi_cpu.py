@@ -125,6 +125,23 @@ def test_gemm_validation_without_device(fp4):
     bn = fp4.QTensorC(0x50000, 0x60000, 0x70000, 128, 256, P(fp4, block_cols=16, scale_mode=2))
     assert L.fp4_gemm_workspace_bytes(ctypes.byref(an), ctypes.byref(bn)) > 0
     assert L.fp4_gemm(ctypes.byref(an), ctypes.byref(bn), c, 0, 128, None, None, None, 0, None) == E.ERR_WORKSPACE
+    # fused output quantization: argument checks (nothing is launched on any error)
+    def run(oq, cq, cptr=c, bb=b):
+        return L.fp4_gemm(ctypes.byref(a), ctypes.byref(bb), cptr, 0, 128,
+                          ctypes.byref(oq) if oq is not None else None,
+                          ctypes.byref(cq) if cq is not None else None, None, 0, None)
+    cq = fp4.QTensorC(0x80000, 0x90000, None, 0, 0, P(fp4))
+    assert run(None, None, cptr=None) == E.ERR_INVALID_ARG            # no output at all
+    assert run(P(fp4), None) == E.ERR_INVALID_ARG                     # out_q without C_q
+    assert run(None, cq) == E.ERR_INVALID_ARG                         # C_q without out_q
+    assert run(P(fp4, block_cols=16), cq) == E.ERR_UNSUPPORTED         # only MX groups of 32
+    assert run(P(fp4, block_cols=16, scale_mode=2), cq) == E.ERR_UNSUPPORTED
+    assert run(P(fp4, hadamard_n=128), cq) == E.ERR_UNSUPPORTED        # no rotation of C
+    assert run(P(fp4, round_mode=5), cq) == E.ERR_INVALID_ARG
+    b100 = qt(100, 256)
+    assert run(P(fp4), cq, bb=b100) == E.ERR_INVALID_ARG               # N % 32 != 0
+    cq_mis = fp4.QTensorC(0x80004, 0x90000, None, 0, 0, P(fp4))
+    assert run(P(fp4), cq_mis) == E.ERR_ALIGNMENT
 
 
 def test_oracle_and_hip_path_share_no_code():

@@ -305,3 +305,49 @@ def test_gemm_shapes(orc, M, N, K, kind):
         pa, pb = P(block=(1, 16), scale_mode=NV46), P(block=(1, 16), scale_mode=NV)
     _gemm_check(orc, A, B, pa, pb)
     _gemm_check(orc, A, B, pa, pb, c_dtype=torch.bfloat16)
+
+
+OUTQ_CASES = [(E2M1, FLOOR, RNE), (E2M1, CEIL, SR), (E4M3, FLOOR, RNE), (E4M3, CEIL, SR)]
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 160, 384), (64, 96, 128), (512, 768, 1024), (300, 544, 512)])
+@pytest.mark.parametrize("kind", ["mxfp4", "mxfp8", "nvfp4"])
+def test_gemm_fused_output_quantize(orc, M, N, K, kind):
+    """The epilogue's MX quantization of C along N equals the oracle's quantization of the very fp32
+    C the same call stores (bit-exact codes and scales, SR included); C itself meets the GEMM bound;
+    skipping C or storing it as bf16 leaves the quantized output unchanged."""
+    rng = np.random.default_rng(M * 7 + N + K)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    if kind == "mxfp4":
+        pa, pb = P(), P(scale_mode=CEIL)
+    elif kind == "mxfp8":
+        pa, pb = P(elem=E4M3), P(elem=E4M3)
+    else:
+        pa, pb = P(block=(1, 16), scale_mode=NV46), P(block=(1, 16), scale_mode=NV)
+    ca, sa, ta = _orc_quant(orc, A, pa)
+    cb, sb, tb = _orc_quant(orc, B, pb)
+    qa = fp4.upload_qtensor(ca, sa, ta, M, K, pa, DEV)
+    qb = fp4.upload_qtensor(cb, sb, tb, N, K, pb, DEV)
+    _gemm_check(orc, A, B, pa, pb)  # the fp32 C of the plain call meets the GEMM bound
+    for elem, sm, rnd in OUTQ_CASES:
+        oq = P(elem=elem, scale_mode=sm, round_mode=rnd, seed=7)
+        c, cq = fp4.gemm(qa, qb, out_dtype=torch.float32, out_q=oq)
+        torch.cuda.synchronize()
+        c_host = c.cpu().numpy()
+        oc, os_, _ = _orc_quant(orc, c_host, oq)
+        gc, gs = cq.codes.cpu().numpy(), cq.scales.cpu().numpy()
+        oc, os_ = oc.reshape(-1), os_.reshape(-1).view(np.uint8)
+        bad = np.nonzero(gc != oc)[0]
+        assert bad.size == 0, f"{(elem, sm, rnd)}: {bad.size} code bytes differ, first at {bad[:8]}"
+        bad = np.nonzero(gs != os_)[0]
+        assert bad.size == 0, f"{(elem, sm, rnd)}: {bad.size} scale bytes differ, first at {bad[:8]}"
+        # the plain call's C is the same fp32 C
+        c_plain = fp4.gemm(qa, qb, out_dtype=torch.float32)
+        assert torch.equal(c_plain.view(torch.int32), c.view(torch.int32))
+        # without C, and with bf16 C: the same codes and scales
+        for kw in (dict(keep_c=False), dict(out_dtype=torch.bfloat16)):
+            c2, cq2 = fp4.gemm(qa, qb, out_q=oq, **kw)
+            torch.cuda.synchronize()
+            assert (c2 is None) == ("keep_c" in kw)
+            assert torch.equal(cq2.codes, cq.codes) and torch.equal(cq2.scales, cq.scales)
