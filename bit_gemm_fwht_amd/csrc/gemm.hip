@@ -594,9 +594,8 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
                         *reinterpret_cast<f32x4*>(smem + row * EP + 4 * col) = (f32x4){v[0], v[1], v[2], v[3]};
                     } else {
                         const int col = wn * 64 + 32 * in + 8 * q + 4 * fg;
-                        const uint32_t w0 = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
-                        const uint32_t w1 = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
-                        *reinterpret_cast<u32x2*>(smem + row * EP + 2 * col) = (u32x2){w0, w1};
+                        *reinterpret_cast<u32x2*>(smem + row * EP + 2 * col) =
+                            (u32x2){pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3])};
                     }
                 }
             }
