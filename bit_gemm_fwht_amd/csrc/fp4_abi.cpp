@@ -316,7 +316,7 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
             if (ldc < N) return FP4_ERR_INVALID_ARG;
             if (!aligned(C, 16)) return FP4_ERR_ALIGNMENT;
         } else {
-            c_dtype = FP4_DT_F32;  // selects the kernel variant only; nothing is stored
+            c_dtype = FP4_DT_BF16;  // selects the kernel variant only; nothing is stored
             ldc = N;
         }
         const int64_t need = gemm_ws(A, B, kind);

@@ -25,6 +25,7 @@
 // even). The MXFP8 product is then scaled by RN(g_A * g_B) in the epilogue.
 #include "device.h"
 #include "fp4_internal.h"
+#include "quant_block.h"
 
 namespace bgf {
 
@@ -530,47 +531,99 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
     char* const cbase = reinterpret_cast<char*>(g.c) + opaque_zero;
     const int64_t Mx = g.M + opaque_zero, Nx = g.N + opaque_zero;
     if constexpr (FQ) {
-        // fused output quantization: tile (im, in) of this wave is one 32-column group of each of
-        // its 32 rows; lane (fr, fg) holds 16 of the group's values (columns 8 q + 4 fg + i), lane
-        // fr + 32 (1 - fg) the other 16
+        // fused output quantization, in two passes of 128 columns: the fp32 values (as an fp32 C
+        // would hold them) are staged in LDS, [256 rows][128] per pass (pass p holds tile in = p
+        // of every wave: staged column 32 wn + j is column 64 wn + 32 p + j of the tile), then one
+        // thread per 32-column group reads its group back and quantizes it with the rules of the
+        // quantize kernels
+        static_assert(C::WTN == 2, "one staged pass per wave tile column");
+        for (int p = 0; p < C::WTN; ++p) {
+            barrier_only();  // every wave is done with the stage buffers / the last pass
 #pragma unroll
-        for (int im = 0; im < C::WTM; ++im)
+            for (int im = 0; im < C::WTM; ++im) {
+                const int row = wm * 128 + 32 * im + fr;
 #pragma unroll
-            for (int in = 0; in < C::WTN; ++in) {
-                const int64_t m = me0 + wm * 128 + 32 * im + fr;
-                const int64_t nb = ne0 + wn * 64 + 32 * in;
-                float v[4][4];
-                float amax = 0.0f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
+                for (int q = 0; q < 4; ++q) {
+                    f32x4 v;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        v[q][i] = NVG ? acc[in][im][4 * q + i] * gscale : acc[in][im][4 * q + i];
-                        amax = fmaxf(amax, fabsf(v[q][i]));
+                        const float a = p == 0 ? acc[0][im][4 * q + i] : acc[C::WTN - 1][im][4 * q + i];
+                        v[i] = NVG ? a * gscale : a;
                     }
-                amax = fmaxf(amax, __shfl_xor(amax, 32));
-                const int k = outq_exp(g, amax);
-                uint32_t part[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) part[q] = outq_encode4(g, v[q], k, m * Nx + nb + 8 * q + 4 * fg);
-                // swap halves with the partner lane so that each lane holds one contiguous half of
-                // the group's codes: lane fg = 0 the first, fg = 1 the second
-                if (g.q_elem == ELEM_E2M1) {
-                    const uint32_t send = fg ? (part[0] | (part[1] << 16)) : (part[2] | (part[3] << 16));
-                    const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
-                    const uint32_t d0 = fg ? ((recv & 0xFFFFu) | (part[2] << 16)) : (part[0] | (recv << 16));
-                    const uint32_t d1 = fg ? ((recv >> 16) | (part[3] << 16)) : (part[1] | (recv & 0xFFFF0000u));
-                    if (m < Mx && nb < Nx)
-                        *reinterpret_cast<u32x2*>(g.qcodes + m * (Nx / 2) + nb / 2 + 8 * fg) = (u32x2){d0, d1};
-                } else {
-                    const uint32_t r0 = (uint32_t)__shfl_xor((int)(fg ? part[0] : part[2]), 32);
-                    const uint32_t r1 = (uint32_t)__shfl_xor((int)(fg ? part[1] : part[3]), 32);
-                    const u32x4 d = fg ? (u32x4){r0, part[2], r1, part[3]} : (u32x4){part[0], r0, part[1], r1};
-                    if (m < Mx && nb < Nx) *reinterpret_cast<u32x4*>(g.qcodes + m * Nx + nb + 16 * fg) = d;
+                    *reinterpret_cast<f32x4*>(smem + row * EP + 4 * (wn * 32 + 8 * q + 4 * fg)) = v;
                 }
-                if (fg == 0 && m < Mx && nb < Nx) g.qscales[m * (Nx / 32) + nb / 32] = (uint8_t)(k + 127);
             }
-        if (!g.c) return;
+            wait_lgkm0();
+            barrier_only();
+#pragma unroll 1
+            for (int t = tid; t < 256 * 4; t += C::NTH) {
+                const int r = t >> 2, j = t & 3;  // row, staged group
+                const int64_t m = me0 + r, nb = ne0 + 64 * j + 32 * p;
+                float v[32];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(smem + r * EP + 4 * (32 * j + 4 * c));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[4 * c + i] = x[i];
+                }
+                uint32_t rw[16], out[8];
+                const float amax = block_amax<32, 0>(v);
+                uint32_t sbyte;
+                if (g.q_round == RND_SR) {
+                    philox_segment(g.q_seed, (uint64_t)(m * Nx + nb), rw);
+                    sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, rw, out)
+                                                  : e8m0_block<ELEM_E4M3, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, rw, out);
+                } else {
+                    sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_RNE, 32, 0>(v, amax, g.q_ceil != 0, rw, out)
+                                                  : e8m0_block<ELEM_E4M3, RND_RNE, 32, 0>(v, amax, g.q_ceil != 0, rw, out);
+                }
+                if (m < Mx && nb < Nx) {
+                    if (g.q_elem == ELEM_E2M1) {
+                        *reinterpret_cast<u32x4*>(g.qcodes + m * (Nx / 2) + nb / 2) = (u32x4){out[0], out[1], out[2], out[3]};
+                    } else {
+                        u32x4* d = reinterpret_cast<u32x4*>(g.qcodes + m * Nx + nb);
+                        d[0] = (u32x4){out[0], out[1], out[2], out[3]};
+                        d[1] = (u32x4){out[4], out[5], out[6], out[7]};
+                    }
+                    g.qscales[m * (Nx / 32) + nb / 32] = (uint8_t)sbyte;
+                }
+            }
+            if (g.c) {
+                // C from the same staged values: 16-byte output pieces, staged column c of a row
+                // is tile column 64 (c / 32) + 32 p + c % 32
+                constexpr int ESZ = OUT == DT_F32 ? 4 : 2, EPC = 16 / ESZ, PPR = 128 / EPC;
+                const bool vec_ok = ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) && ((ldc * ESZ) % 16 == 0);
+#pragma unroll 1
+                for (int t = tid; t < 256 * PPR; t += C::NTH) {
+                    const int r = t / PPR, c = (t % PPR) * EPC;
+                    const int64_t m = me0 + r, n = ne0 + 64 * (c >> 5) + 32 * p + (c & 31);
+                    if (m >= Mx) continue;
+                    const float* src = reinterpret_cast<const float*>(smem + r * EP) + c;
+                    u32x4 val;
+                    if constexpr (OUT == DT_F32) {
+                        val = *reinterpret_cast<const u32x4*>(src);
+                    } else {
+                        const f32x4 a = *reinterpret_cast<const f32x4*>(src), b = *reinterpret_cast<const f32x4*>(src + 4);
+                        val = (u32x4){pack_bf16x2_rne(a[0], a[1]), pack_bf16x2_rne(a[2], a[3]),
+                                      pack_bf16x2_rne(b[0], b[1]), pack_bf16x2_rne(b[2], b[3])};
+                    }
+                    char* cp = cbase + (m * ldc + n) * ESZ;
+                    if (vec_ok && n + EPC <= Nx) {
+                        *reinterpret_cast<u32x4*>(cp) = val;
+                    } else {
+                        for (int i = 0; i < EPC; ++i) {
+                            if (n + i < Nx) {
+                                if constexpr (OUT == DT_F32)
+                                    reinterpret_cast<uint32_t*>(cp)[i] = val[i];
+                                else
+                                    reinterpret_cast<uint16_t*>(cp)[i] = (uint16_t)(val[i >> 1] >> (16 * (i & 1)));
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        return;
     }
     constexpr int ESZ = OUT == DT_F32 ? 4 : 2;
     // 16-byte stores need a 16-byte aligned row start

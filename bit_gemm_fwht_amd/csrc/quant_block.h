@@ -1,0 +1,119 @@
+// Per-block quantization steps shared by the quantize kernels and the GEMM's fused output
+// quantization: block amax, Philox words for stochastic rounding, and the element encode under a
+// power-of-two (E8M0) or general scale. A block is B consecutive values of a lane's 32-element
+// segment v, starting at OFF.
+#pragma once
+#include "device.h"
+#include "fp4_internal.h"
+
+namespace bgf {
+
+template <int B, int OFF>
+__device__ __forceinline__ float block_amax(const float (&v)[32]) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = OFF; i < OFF + B; ++i) m = fmaxf(m, fabsf(v[i]));
+    return m;
+}
+
+// Philox words for elements idx0 .. idx0 + 31 (idx0 a multiple of 32): u16 for element j is the
+// low (even j) / high (odd j) half of word (j >> 1) & 3 of the call for counter (idx0 + j) >> 3.
+__device__ __forceinline__ void philox_segment(uint64_t seed, uint64_t idx0, uint32_t (&w)[16]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint64_t ctr = (idx0 >> 3) + (uint64_t)g;
+        uint32_t c0 = (uint32_t)ctr, c1 = (uint32_t)(ctr >> 32), c2 = 0u, c3 = 0u;
+        philox4x32_10(c0, c1, c2, c3, (uint32_t)seed, (uint32_t)(seed >> 32));
+        w[4 * g + 0] = c0;
+        w[4 * g + 1] = c1;
+        w[4 * g + 2] = c2;
+        w[4 * g + 3] = c3;
+    }
+}
+__device__ __forceinline__ uint32_t sr_u16(const uint32_t (&w)[16], int j) {
+    const uint32_t word = w[j >> 1];
+    return (j & 1) ? (word >> 16) : (word & 0xFFFFu);
+}
+
+// Encode elements [OFF, OFF + B) of v into out (nibbles for E2M1: element j -> nibble j of the
+// 16-byte segment; bytes for E4M3). Scale arguments:
+//  pow2: the block scale is 2^k (k >= -126 after the caller's adjustment): the hardware convert
+//        divides by it exactly (RNE); SR multiplies by rcp = 2^-k exactly.
+//  else: elements are v * rcp (RN), converted with scale 1.
+template <int ELEM, int RND, int B, int OFF>
+__device__ __forceinline__ void encode_block(float (&v)[32], bool pow2, float cvt_scale, float rcp,
+                                             float clampv, const uint32_t (&rw)[16],
+                                             uint32_t (&out)[8]) {
+    if constexpr (RND == RND_RNE) {
+        if (!pow2) {
+#pragma unroll
+            for (int i = OFF; i < OFF + B; ++i) v[i] = v[i] * rcp;
+        }
+        if constexpr (ELEM == ELEM_E2M1) {
+#pragma unroll
+            for (int w = OFF / 8; w < (OFF + B) / 8; ++w) {
+                uint32_t r = 0u;
+                r = cvt_fp4x2<0>(r, v[8 * w + 0], v[8 * w + 1], cvt_scale);
+                r = cvt_fp4x2<1>(r, v[8 * w + 2], v[8 * w + 3], cvt_scale);
+                r = cvt_fp4x2<2>(r, v[8 * w + 4], v[8 * w + 5], cvt_scale);
+                r = cvt_fp4x2<3>(r, v[8 * w + 6], v[8 * w + 7], cvt_scale);
+                out[w] = r;
+            }
+        } else {
+#pragma unroll
+            for (int w = OFF / 4; w < (OFF + B) / 4; ++w) {
+                // saturate at +-448 (times the scale) before the non-saturating convert
+                const float a0 = __builtin_amdgcn_fmed3f(v[4 * w + 0], -clampv, clampv);
+                const float a1 = __builtin_amdgcn_fmed3f(v[4 * w + 1], -clampv, clampv);
+                const float a2 = __builtin_amdgcn_fmed3f(v[4 * w + 2], -clampv, clampv);
+                const float a3 = __builtin_amdgcn_fmed3f(v[4 * w + 3], -clampv, clampv);
+                uint32_t r = 0u;
+                r = cvt_fp8x2<false>(r, a0, a1, cvt_scale);
+                r = cvt_fp8x2<true>(r, a2, a3, cvt_scale);
+                out[w] = r;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = OFF; i < OFF + B; ++i) v[i] = v[i] * rcp;
+        if constexpr (ELEM == ELEM_E2M1) {
+#pragma unroll
+            for (int w = OFF / 8; w < (OFF + B) / 8; ++w) {
+                uint32_t r = 0u;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) r |= e2m1_sr(v[8 * w + j], sr_u16(rw, 8 * w + j)) << (4 * j);
+                out[w] = r;
+            }
+        } else {
+#pragma unroll
+            for (int w = OFF / 4; w < (OFF + B) / 4; ++w) {
+                uint32_t r = 0u;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) r |= e4m3_sr(v[4 * w + j], sr_u16(rw, 4 * w + j)) << (8 * j);
+                out[w] = r;
+            }
+        }
+    }
+}
+
+// E8M0 path for one block: returns the scale byte; encodes into out.
+template <int ELEM, int RND, int B, int OFF>
+__device__ __forceinline__ uint32_t e8m0_block(float (&v)[32], float amax, bool ceil_rule,
+                                               const uint32_t (&rw)[16], uint32_t (&out)[8]) {
+    int k = (ELEM == ELEM_E2M1) ? e8m0_exp<2, 0x400000u>(amax, ceil_rule)
+                                : e8m0_exp<8, 0x600000u>(amax, ceil_rule);
+    const uint32_t sbyte = (uint32_t)(k + 127);
+    if (k == -127) {
+        // 2^-127 is not a normal fp32: divide by 2^-126 after doubling (exact for such tiny x)
+#pragma unroll
+        for (int i = OFF; i < OFF + B; ++i) v[i] = v[i] * 2.0f;
+        k = -126;
+    }
+    const float scale = pow2f(k);
+    const float rcp = __builtin_amdgcn_ldexpf(1.0f, -k);
+    const float clampv = 448.0f * scale;
+    encode_block<ELEM, RND, B, OFF>(v, true, scale, rcp, clampv, rw, out);
+    return sbyte;
+}
+
+}  // namespace bgf
