@@ -171,6 +171,58 @@ int fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int
     }
 }
 
+int fp4_quantize_colwise(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                         const fp4_qparams* p, void* codes, void* scales, float* tensor_scale,
+                         void* workspace, int64_t ws_bytes, void* stream) {
+    try {
+        // the quantized tensor is T = x^T: cols x rows, groups along x's rows
+        Layout lay;
+        int rc = check_params(cols, rows, p, &lay);
+        if (rc != FP4_OK) return rc;
+        if (lay != L_SEG1D) return FP4_ERR_UNSUPPORTED;
+        if (!x || !codes || !scales) return FP4_ERR_INVALID_ARG;
+        if (x_dtype != FP4_DT_F32 && x_dtype != FP4_DT_BF16) return FP4_ERR_INVALID_ARG;
+        if (ldx < cols) return FP4_ERR_INVALID_ARG;
+        if (codes == x || scales == x || codes == scales) return FP4_ERR_INVALID_ARG;
+        if (is_nv(p->scale_mode) && !tensor_scale) return FP4_ERR_INVALID_ARG;
+        const int esz = x_dtype == FP4_DT_BF16 ? 2 : 4;
+        if (!aligned(x, 16) || (ldx * esz) % 16 || !aligned(codes, 16) || !aligned(scales, 8))
+            return FP4_ERR_ALIGNMENT;
+        // tile offsets are 32-bit: 256 rows of x must span less than 2 GiB
+        if (256 * ldx * esz >= (int64_t(1) << 31)) return FP4_ERR_UNSUPPORTED;
+        const int64_t need = ws_bytes_needed(lay, p);
+        if (need && (!workspace || ws_bytes < need)) return FP4_ERR_WORKSPACE;
+        if (need && !aligned(workspace, 4)) return FP4_ERR_ALIGNMENT;
+
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        const int sc = scale_class(p->scale_mode);
+        uint32_t* ws = reinterpret_cast<uint32_t*>(workspace);
+        SegArgs a{};
+        a.x = x;
+        a.rows = cols;  // T's shape
+        a.cols = rows;
+        a.ldx = ldx;
+        a.nseg = cols * (rows / 32);
+        a.codes = reinterpret_cast<uint8_t*>(codes);
+        a.scales = scales;
+        a.tensor_scale = tensor_scale;
+        a.ws = ws;
+        a.seed = p->seed;
+        a.ceil_rule = p->scale_mode == FP4_SCALE_E8M0_CEIL;
+        a.four_six = p->scale_mode == FP4_SCALE_NV_4OVER6;
+        a.colwise = 1;
+        if (sc == SC_NV) {
+            if ((rc = hip_status(launch_zero_u32(ws, 1, s))) != FP4_OK) return rc;
+            rc = hip_status(launch_segment(a, x_dtype, p->hadamard_n, p->elem, sc, p->round_mode, 1, 32, PASS_AMAX, s));
+            if (rc != FP4_OK) return rc;
+        }
+        return hip_status(launch_segment(a, x_dtype, p->hadamard_n, p->elem, sc, p->round_mode, 1,
+                                         p->block_cols, PASS_QUANT, s));
+    } catch (...) {
+        return FP4_ERR_INTERNAL;
+    }
+}
+
 int fp4_dequantize(const void* codes, const void* scales, const float* tensor_scale, int64_t rows,
                    int64_t cols, const fp4_qparams* p, void* y, int32_t y_dtype, int64_t ldy,
                    void* stream) {

@@ -24,6 +24,8 @@ struct SegArgs {
     uint64_t seed;
     int ceil_rule;
     int four_six;
+    // column-wise view: rows x cols describe T = x^T, x is [cols, rows] with row pitch ldx
+    int colwise;
 };
 
 struct RowArgs {

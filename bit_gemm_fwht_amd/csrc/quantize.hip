@@ -104,6 +104,55 @@ __device__ __forceinline__ void load_wave_segments_1d(const SegArgs& a, int64_t 
     }
 }
 
+// Column-wise view: the logical tensor is T = x^T ([rows, cols] of SegArgs describe T; x is
+// [cols, rows] with row pitch ldx). A workgroup tile is TCW = 4 * 64 / SEGW consecutive T-rows (x
+// columns) by SEGW consecutive segments (32 SEGW x rows). Wave w takes T-rows w * 64 / SEGW ..,
+// and lane l of it T-row l / SEGW of those and segment l % SEGW, so the segments of one Hadamard
+// chunk (up to SEGW) sit in lanes l ^ 1, l ^ 2, (l ^ 4). The workgroup reads the tile's x rows
+// with 16-byte loads (each row piece TCW elements long: whole cache lines), stores them in LDS as
+// SEGW blocks of 32 rows (each block skewed by 8 dwords, so that the column reads below hit
+// distinct banks), and each lane then reads its column of 32 values. Every thread of the
+// workgroup must call it (it holds a barrier).
+template <int IN, int SEGW>
+__device__ __forceinline__ void load_block_segments_t(const SegArgs& a, int64_t tt, int64_t ts, uint8_t* lds,
+                                                      float (&v)[32]) {
+    constexpr int P = SegIO<IN>::P, ESZ = SegIO<IN>::ESZ, TCW = 4 * 64 / SEGW, PITCH = TCW * ESZ;
+    constexpr int PPR = PITCH / 16, BSTR = 32 * PITCH + 32;
+    static_assert(32 * SEGW * PPR == kThreads * P, "tile pieces per thread");
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t x0 = (ts * SEGW * 32) * a.ldx + tt * TCW;  // first element of the tile in x
+    const int64_t total = a.cols * a.ldx;                     // elements of x (T-columns are x rows)
+    int64_t left = (total - x0) * ESZ;
+    left = left < 0 ? 0 : (left > 0x7FFFFFFF ? 0x7FFFFFFF : left);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(a.x) + (left > 0 ? x0 * ESZ : 0)), (short)0, (int)left, 0x00020000);
+    u32x4 raw[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int ch = kThreads * i + tid, rho = ch / PPR, q = ch % PPR;
+        // pieces that start at or past x's last column read zeros; x rows past the end lie past
+        // the buffer's extent and read zeros too
+        const bool colok = tt * TCW + (16 * q) / ESZ < a.rows;
+        raw[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, colok ? (int)(rho * a.ldx * ESZ + 16 * q) : -1, 0, 2 /* nt */);
+    }
+    __syncthreads();  // the previous tile's column reads are done
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int ch = kThreads * i + tid, rho = ch / PPR, q = ch % PPR;
+        *reinterpret_cast<u32x4*>(lds + (rho / 32) * BSTR + (rho % 32) * PITCH + 16 * q) = raw[i];
+    }
+    __syncthreads();
+    const int j = wv * (64 / SEGW) + lane / SEGW, sg = lane % SEGW;
+    const uint8_t* col = lds + sg * BSTR + j * ESZ;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+        if constexpr (IN == DT_BF16)
+            v[r] = __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(col + r * PITCH)) << 16);
+        else
+            v[r] = *reinterpret_cast<const float*>(col + r * PITCH);
+    }
+}
+
 // Blockwise H_n / sqrt(n) on the segment (see the file comment for the lane mapping).
 template <int HN>
 __device__ __forceinline__ void fwht_segment(float (&v)[32]) {
@@ -203,10 +252,13 @@ __device__ __forceinline__ float f32_block(float (&v)[32], float amax, const uin
 // ---------------------------------------------------------------------------------------------
 // The segment kernel (1D groups, 2D tiles, amax pass, rotation pass)
 // ---------------------------------------------------------------------------------------------
-template <int IN, int HN, int ELEM, int SC, int RND, int BR, int BC, int PASS>
+template <int IN, int HN, int ELEM, int SC, int RND, int BR, int BC, int PASS, bool TRX>
 __global__ __launch_bounds__(kThreads) void k_segment(SegArgs a) {
     constexpr int P = SegIO<IN>::P, ESZ = SegIO<IN>::ESZ;
-    __shared__ u32x4 stage[kThreads / 64][64 * P];
+    // column-wise view: workgroup tiles of TCW T-rows x SEGW segments (see load_block_segments_t)
+    constexpr int SEGW = HN >= 256 ? 8 : 4, TCW = 4 * 64 / SEGW;
+    static_assert(!TRX || (BR == 1 && PASS != PASS_ROTATE), "column-wise view: 1D groups only");
+    __shared__ u32x4 stage[kThreads / 64][64 * P + (TRX ? 16 : 0)];
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;  // wave-uniform wv
     const int64_t spr = a.cols >> 5;  // segments per row
 
@@ -214,11 +266,21 @@ __global__ __launch_bounds__(kThreads) void k_segment(SegArgs a) {
         // tensor amax of the (rotated) input: a grid-stride walk over 256-segment groups, one
         // atomic max per workgroup (non-negative floats order like their bit patterns)
         float m = 0.0f;
-        for (int64_t g0 = (int64_t)blockIdx.x * kThreads; g0 < a.nseg; g0 += (int64_t)gridDim.x * kThreads) {
-            float v[32];
-            load_wave_segments_1d<IN>(a, g0 + 64 * wv, stage[wv], v);
-            fwht_segment<HN>(v);
-            m = fmaxf(m, block_amax<32, 0>(v));
+        if constexpr (TRX) {
+            const int64_t ntt = (a.rows + TCW - 1) / TCW, ntiles = ntt * ((spr + SEGW - 1) / SEGW);
+            for (int64_t w = blockIdx.x; w < ntiles; w += gridDim.x) {  // workgroup-uniform
+                float v[32];
+                load_block_segments_t<IN, SEGW>(a, w % ntt, w / ntt, reinterpret_cast<uint8_t*>(&stage[0][0]), v);
+                fwht_segment<HN>(v);
+                m = fmaxf(m, block_amax<32, 0>(v));  // lanes outside the tensor hold zeros
+            }
+        } else {
+            for (int64_t g0 = (int64_t)blockIdx.x * kThreads; g0 < a.nseg; g0 += (int64_t)gridDim.x * kThreads) {
+                float v[32];
+                load_wave_segments_1d<IN>(a, g0 + 64 * wv, stage[wv], v);
+                fwht_segment<HN>(v);
+                m = fmaxf(m, block_amax<32, 0>(v));
+            }
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -239,7 +301,15 @@ __global__ __launch_bounds__(kThreads) void k_segment(SegArgs a) {
     int64_t seg, row = 0, sc = 0;
     bool valid;
     float v[32];
-    if constexpr (BR == 1) {
+    if constexpr (TRX) {
+        const int64_t ntt = (a.rows + TCW - 1) / TCW;
+        const int64_t tt = blockIdx.x % ntt, ts = blockIdx.x / ntt;
+        const int64_t tr = tt * TCW + wv * (64 / SEGW) + lane / SEGW;
+        sc = ts * SEGW + lane % SEGW;
+        valid = tr < a.rows && sc < spr;
+        seg = tr * spr + sc;
+        load_block_segments_t<IN, SEGW>(a, tt, ts, reinterpret_cast<uint8_t*>(&stage[0][0]), v);
+    } else if constexpr (BR == 1) {
         const int64_t wbase = (int64_t)blockIdx.x * kThreads + 64 * wv;
         seg = wbase + lane;
         valid = seg < a.nseg;
@@ -569,13 +639,23 @@ __global__ __launch_bounds__(kThreads) void k_dequant_rowblock(DeqArgs a) {
 
 template <int IN, int HN, int ELEM, int SC, int RND, int BR, int BC>
 static hipError_t launch_seg_q(const SegArgs& a, int pass, hipStream_t stream) {
+    if (a.colwise) {
+        if constexpr (BR == 1) {
+            constexpr int SEGW = HN >= 256 ? 8 : 4, TCW = 4 * 64 / SEGW;
+            const int64_t grid = ((a.rows + TCW - 1) / TCW) * (((a.cols >> 5) + SEGW - 1) / SEGW);
+            if (pass == PASS_AMAX)
+                BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, 32, PASS_AMAX, true>), (grid < 1024 ? grid : 1024), a);
+            BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, BC, PASS_QUANT, true>), grid, a);
+        }
+        return hipErrorInvalidValue;
+    }
     int64_t grid;
     if (BR == 1) grid = (a.nseg + kThreads - 1) / kThreads;
     else grid = (a.rows / 32) * (((a.cols >> 5) + 7) >> 3);
     // the amax pass walks the tensor with at most 1024 workgroups (one atomic each)
-    if (pass == PASS_AMAX) BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, 32, PASS_AMAX>), (grid < 1024 ? grid : 1024), a);
-    if (pass == PASS_ROTATE) BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, 32, PASS_ROTATE>), grid, a);
-    BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, BR, BC, PASS_QUANT>), grid, a);
+    if (pass == PASS_AMAX) BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, 32, PASS_AMAX, false>), (grid < 1024 ? grid : 1024), a);
+    if (pass == PASS_ROTATE) BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, 32, PASS_ROTATE, false>), grid, a);
+    BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, BR, BC, PASS_QUANT, false>), grid, a);
 }
 
 template <int IN, int HN>

@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         getattr(L, name).restype = I64
     L.fp4_quantize.argtypes = [P, I32, I64, I64, I64, QP, P, P, P, P, I64, P]
     L.fp4_quantize.restype = ctypes.c_int
+    L.fp4_quantize_colwise.argtypes = [P, I32, I64, I64, I64, QP, P, P, P, P, I64, P]
+    L.fp4_quantize_colwise.restype = ctypes.c_int
     L.fp4_dequantize.argtypes = [P, P, P, I64, I64, QP, P, I32, I64, P]
     L.fp4_dequantize.restype = ctypes.c_int
     L.fp4_hadamard.argtypes = [P, I32, I64, I64, I64, I32, P, P]
@@ -171,6 +173,30 @@ def quantize(x: torch.Tensor, params: Params = MXFP4, out: QTensor | None = None
                             workspace.numel() if workspace is not None else 0,
                             _stream_ptr(x.device))
     _check(st, "fp4_quantize")
+    return q
+
+
+def quantize_colwise(x: torch.Tensor, params: Params = MXFP4, out: QTensor | None = None,
+                     workspace: torch.Tensor | None = None) -> QTensor:
+    """Quantize x^T (shape [cols, rows]) along its last axis, i.e. x along its first axis, without
+    forming the transpose. Returns the QTensor of the cols x rows tensor."""
+    if x.dim() != 2 or not x.is_cuda:
+        raise ValueError("x must be a 2-D CUDA tensor")
+    if x.stride(1) != 1:
+        raise ValueError("x must be contiguous along its last axis")
+    rows, cols = x.shape
+    q = out if out is not None else empty_qtensor(cols, rows, params, x.device)
+    _, _, wb = buffer_sizes(cols, rows, params)
+    if wb and workspace is None:
+        workspace = torch.empty(wb, dtype=torch.uint8, device=x.device)
+    p = params.c()
+    ts = q.tensor_scale.data_ptr() if q.tensor_scale is not None else None
+    st = lib().fp4_quantize_colwise(x.data_ptr(), _dtype_code(x), rows, cols, x.stride(0),
+                                    ctypes.byref(p), q.codes.data_ptr(), q.scales.data_ptr(), ts,
+                                    workspace.data_ptr() if workspace is not None else None,
+                                    workspace.numel() if workspace is not None else 0,
+                                    _stream_ptr(x.device))
+    _check(st, "fp4_quantize_colwise")
     return q
 
 

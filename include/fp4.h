@@ -129,6 +129,19 @@ int fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int
                  const fp4_qparams* p, void* codes, void* scales, float* tensor_scale,
                  void* workspace, int64_t ws_bytes, void* stream);
 
+/* Column-wise quantization: quantize T = x^T without forming it. x is [rows, cols] (row pitch ldx);
+ * the result is exactly fp4_quantize of the [cols, rows] tensor T with *p: codes, scales and the
+ * rotation run along x's rows (T's contiguous axis), e.g. to feed dW = dY^T X, whose contraction
+ * runs over the token axis (the backward pass of the Quartet notes' recipe; the transposition-
+ * invariant blocks of "Stable FP4 Training via Transposition-Invariant Block Quantization" exist so
+ * that a weight quantized once serves both orientations). Sizes and layouts are those of a cols x
+ * rows tensor (fp4_codes_bytes(cols, rows, p), ...). Supported: 1D groups (block_rows == 1,
+ * block_cols 16 or 32; rows % 32 == 0), every scale, rounding and Hadamard mode fp4_quantize
+ * accepts for them; other blocks return FP4_ERR_UNSUPPORTED. Alignment as for fp4_quantize. */
+int fp4_quantize_colwise(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                         const fp4_qparams* p, void* codes, void* scales, float* tensor_scale,
+                         void* workspace, int64_t ws_bytes, void* stream);
+
 /* y = RN(val(q) * d) for every element (d the decoded block scale: 2^k, the fp32 scale, or
  * RN(E4M3(s) * g) in the NVFP4 modes), then the rotation again when p->hadamard_n > 0 (H/sqrt(n)
  * is its own inverse). y: [rows, cols] fp32 or bf16 (round to nearest even), leading dim ldy. */

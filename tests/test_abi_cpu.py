@@ -159,3 +159,25 @@ def test_oracle_and_hip_path_share_no_code():
                     if s.startswith(("#include", "import ", "from ")):
                         for b in banned:
                             assert b not in s, f"{f}: {s}"
+
+
+def _quant_cw(fp4, p, rows=256, cols=64, x=0x1000, codes=0x2000, scales=0x3000, ts=None, ws=None,
+              wsb=0, ldx=None, dtype=1):
+    return fp4.lib().fp4_quantize_colwise(x, dtype, rows, cols, ldx or cols, ctypes.byref(p), codes,
+                                          scales, ts, ws, wsb, None)
+
+
+def test_quantize_colwise_validation_without_device(fp4):
+    """The column-wise call checks the transposed shape (cols x rows, groups along x's rows)."""
+    E = fp4
+    assert _quant_cw(fp4, P(fp4), x=None) == E.ERR_INVALID_ARG
+    assert _quant_cw(fp4, P(fp4), rows=250) == E.ERR_INVALID_ARG          # T has 250 columns
+    assert _quant_cw(fp4, P(fp4, hadamard_n=128), rows=320) == E.ERR_INVALID_ARG
+    assert _quant_cw(fp4, P(fp4, block_rows=32)) == E.ERR_UNSUPPORTED      # 2D tiles
+    assert _quant_cw(fp4, P(fp4, block_cols=256)) == E.ERR_UNSUPPORTED     # per-row of T
+    assert _quant_cw(fp4, P(fp4, scale_mode=2, block_cols=16)) == E.ERR_INVALID_ARG  # no tensor_scale
+    assert _quant_cw(fp4, P(fp4, scale_mode=2, block_cols=16), ts=0x4000) == E.ERR_WORKSPACE
+    assert _quant_cw(fp4, P(fp4), x=0x1004) == E.ERR_ALIGNMENT
+    assert _quant_cw(fp4, P(fp4), ldx=66) == E.ERR_ALIGNMENT
+    assert _quant_cw(fp4, P(fp4), ldx=32) == E.ERR_INVALID_ARG            # ldx < cols
+    assert _quant_cw(fp4, P(fp4), codes=0x1000) == E.ERR_INVALID_ARG      # aliasing

@@ -351,3 +351,78 @@ def test_gemm_fused_output_quantize(orc, M, N, K, kind):
             torch.cuda.synchronize()
             assert (c2 is None) == ("keep_c" in kw)
             assert torch.equal(cq2.codes, cq.codes) and torch.equal(cq2.scales, cq.scales)
+
+
+CW_CASES = [
+    # dtype, rows, cols, params
+    ("bf16", 256, 64, dict()),
+    ("bf16", 384, 200, dict(hadamard_n=128)),
+    ("f32", 96, 48, dict(hadamard_n=32, scale_mode=CEIL, round_mode=SR, seed=7)),
+    ("bf16", 512, 72, dict(hadamard_n=256, round_mode=SR, scale_mode=CEIL, seed=3)),
+    ("bf16", 256, 104, dict(elem=E4M3, hadamard_n=64)),
+    ("f32", 128, 40, dict(block=(1, 16), scale_mode=NV46)),
+    ("bf16", 256, 64, dict(block=(1, 16), scale_mode=NV, hadamard_n=128)),
+    ("bf16", 160, 40, dict(block=(1, 16), scale_mode=F32, round_mode=SR, seed=11)),
+    ("f32", 64, 132, dict(scale_mode=F32, hadamard_n=16)),
+]
+
+
+@pytest.mark.parametrize("dt,rows,cols,kw", CW_CASES)
+def test_quantize_colwise_parity(orc, dt, rows, cols, kw):
+    """Column-wise quantization of x equals the oracle's quantization of x^T, bit for bit (also
+    with a row pitch wider than the row)."""
+    rng = np.random.default_rng(rows * 31 + cols)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x[rng.integers(rows), rng.integers(cols)] *= 40.0
+    params = P(**kw)
+    xt = np.ascontiguousarray(x.T)
+    if dt == "bf16":
+        xb = wl.f32_to_bf16_bits(x)
+        xt_in = np.ascontiguousarray(xb.T)
+        dev = _to_dev(xb)
+    else:
+        xt_in = xt
+        dev = _to_dev(x)
+    oc, os_, ots = _orc_quant(orc, xt_in, params)
+    for pitch in (0, 24):
+        if pitch:
+            wide = torch.zeros(rows, cols + pitch, dtype=dev.dtype, device=DEV)
+            wide[:, :cols] = dev
+            src = wide[:, :cols]
+        else:
+            src = dev
+        q = fp4.quantize_colwise(src, params)
+        torch.cuda.synchronize()
+        assert q.rows == cols and q.cols == rows
+        gc, gs = q.codes.cpu().numpy(), q.scales.cpu().numpy()
+        bad = np.nonzero(gc != oc.reshape(-1))[0]
+        assert bad.size == 0, f"pitch {pitch}: {bad.size} code bytes differ, first at {bad[:8]}"
+        bad = np.nonzero(gs != os_.reshape(-1).view(np.uint8))[0]
+        assert bad.size == 0, f"pitch {pitch}: {bad.size} scale bytes differ, first at {bad[:8]}"
+        if ots is not None:
+            assert q.tensor_scale.cpu().numpy().view(np.uint32)[0] == ots.view(np.uint32)[0]
+
+
+def test_weight_gradient_gemm_colwise(orc):
+    """dW = dY^T X for a backward step: both operands quantized column-wise (the contraction runs
+    over the 512 tokens), then the block-scaled GEMM; checked against the fp64 product of the
+    oracle's quantization of dY^T and X^T."""
+    rng = np.random.default_rng(5)
+    T, N, K = 512, 288, 320  # tokens, output features, input features
+    dy = (rng.standard_t(3, (T, N)) * 1e-3).astype(np.float32)
+    xx = rng.standard_normal((T, K)).astype(np.float32)
+    pa = P(hadamard_n=128, scale_mode=CEIL, round_mode=SR, seed=7)
+    pb = P(hadamard_n=128)
+    qa = fp4.quantize_colwise(_to_dev(wl.f32_to_bf16_bits(dy)), pa)
+    qb = fp4.quantize_colwise(_to_dev(wl.f32_to_bf16_bits(xx)), pb)
+    dw = fp4.gemm(qa, qb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ca, sa, _ = _orc_quant(orc, np.ascontiguousarray(wl.f32_to_bf16_bits(dy).T), pa)
+    cb, sb, _ = _orc_quant(orc, np.ascontiguousarray(wl.f32_to_bf16_bits(xx).T), pb)
+    assert np.array_equal(qa.codes.cpu().numpy(), ca.reshape(-1))
+    assert np.array_equal(qb.codes.cpu().numpy(), cb.reshape(-1))
+    a64 = orc.operand_f64(ca, sa, None, N, T)
+    b64 = orc.operand_f64(cb, sb, None, K, T)
+    ref, sabs = orc.gemm_f64(a64, b64)
+    err = np.abs(dw.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= 1e-5 * sabs + 1e-30)
