@@ -23,6 +23,8 @@
 // matrix core takes: per group, with S the larger of its two block scales, E is the smallest
 // exponent with 448 * 2^E >= 6 S and every element becomes E4M3(val(q) * s_blk * 2^-E) (nearest
 // even). The MXFP8 product is then scaled by RN(g_A * g_B) in the epilogue.
+#include <type_traits>
+
 #include "device.h"
 #include "fp4_internal.h"
 #include "quant_block.h"
@@ -387,17 +389,25 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
         }
     }
 
-    auto issue = [&](int kt) {
+    // The copies of a stage are issued in NKK parts, one per 64-deep MFMA step of the previous
+    // stage, so that no wave stalls on a full address FIFO with all its copies at once (part p:
+    // A and B copies i in [p IPW / NKK, (p + 1) IPW / NKK); the scales with part 0).
+    static_assert(C::IPW % C::NKK == 0, "copies per step");
+    // Stage KT (one past the last) is a dummy: its offsets lie past every buffer's extent, so the
+    // copies read nothing and write zeros into the free stage buffer.
+    auto issue_part = [&](int kt, int part) {
         uint8_t* st = smem + (kt % C::NST) * C::STAGE;
-        const int so = kt * C::RB, ss = kt * C::SPR;
+        const int so = kt < KT ? kt * C::RB : (1 << 30), ss = kt < KT ? kt * C::SPR : (1 << 30);
+        constexpr int IPP = C::IPW / C::NKK;
 #pragma unroll
-        for (int i = 0; i < C::IPW; ++i)
+        for (int ii = 0; ii < IPP; ++ii) {
+            const int i = part * IPP + ii;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(st + C::OFF_A + (wave * C::IPW + i) * 1024), 16,
                                                      voA[i & 1], so + (int)(8 * i * rowbytes), 0, 0);
-#pragma unroll
-        for (int i = 0; i < C::IPW; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(st + C::OFF_B + (wave * C::IPW + i) * 1024),
                                                      16, voB[i & 1], so + (int)(8 * i * rowbytes), 0, 0);
+        }
+        if (part != 0) return;
 #pragma unroll
         for (int j = 0; j < C::SPW; ++j) {
             if ((wave * C::SPW + j) * 64 >= C::SB / 4)  // wave-uniform
@@ -407,6 +417,10 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_ptr_t)(st + (wave * C::SPW + j) * 256),
                                                          4, voS[j], ss, 0, 0);
         }
+    };
+    auto issue = [&](int kt) {
+#pragma unroll
+        for (int p = 0; p < C::NKK; ++p) issue_part(kt, p);
     };
 
     v16f acc[C::WTN][C::WTM];
@@ -458,7 +472,8 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
         for (int i = 0; i < C::WTN; ++i)
             fb[i] = frag(st + bRow + 32 * C::RB * i + ch[kk][0], st + bRow + 32 * C::RB * i + ch[kk][NP - 1]);
     };
-    auto compute = [&](const uint8_t* st) {
+    // one stage's MFMAs, with the copies of stage `next` issued along the way
+    auto compute = [&](const uint8_t* st, int next) {
         int sa[C::WTM][C::SPR / 4], sb[C::WTN][C::SPR / 4];
 #pragma unroll
         for (int i = 0; i < C::WTM; ++i)
@@ -475,6 +490,7 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
 #pragma unroll
         for (int kk = 0; kk < C::NKK; ++kk) {
             const int cur = kk & 1, nxt = cur ^ 1;
+            issue_part(next, kk);
             if (kk + 1 < C::NKK) load_frags(st, kk + 1, fa[nxt], fb[nxt]);
             // scale byte of group 2 kk + (l / 32): dword kk / 2 after the lane shift, byte 2 (kk % 2)
 #pragma unroll
@@ -490,8 +506,10 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
                             fb[cur][in], fa[cur][im], acc[in][im], FP8 ? 0 : 4, FP8 ? 0 : 4, 2,
                             sb[in][kk >> 1], 2, sa[im][kk >> 1]);
                 }
-            // issue the next step's reads first, then this step's MFMAs; nothing moves across
-            // step boundaries
+            // issue this step's part of the next stage's copies, the next step's reads, then this
+            // step's MFMAs; nothing moves across step boundaries
+            if (kk == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2 * (C::IPW / C::NKK) + C::SPW, 0);
+            else __builtin_amdgcn_sched_group_barrier(0x020, 2 * (C::IPW / C::NKK), 0);
             if (kk + 1 < C::NKK) __builtin_amdgcn_sched_group_barrier(0x100, (C::WTM + C::WTN) * NP, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, C::WTM * C::WTN, 0);
             __builtin_amdgcn_sched_barrier(0);
@@ -506,11 +524,11 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
             if (kt < KT) {
                 wait_vm<0>();    // this wave's copies of stage kt have landed
                 barrier_only();  // ... and everyone's; stage kt-1 is no longer read
-                if (kt + 1 < KT) issue(kt + 1);
-                compute(smem + s * C::STAGE);
+                compute(smem + s * C::STAGE, kt + 1);
             }
         }
     }
+    wait_vm<0>();  // the dummy stage's zero-fill has landed before the LDS is reused
 
     // Epilogue, staged through LDS so that every global store writes whole 16-byte pieces of a
     // row and consecutive lanes cover consecutive bytes. Lane (fr, fg) holds, for 4-register group
