@@ -18,7 +18,12 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool valid_hn(int n) { return n == 0 || n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
 
-bool is_nv(int sm) { return sm == FP4_SCALE_NV || sm == FP4_SCALE_NV_4OVER6; }
+bool is_nv(int sm) {
+    return sm == FP4_SCALE_NV || sm == FP4_SCALE_NV_4OVER6 || sm == FP4_SCALE_NV_GIVEN ||
+           sm == FP4_SCALE_NV_4OVER6_GIVEN;
+}
+bool is_4over6(int sm) { return sm == FP4_SCALE_NV_4OVER6 || sm == FP4_SCALE_NV_4OVER6_GIVEN; }
+bool is_given(int sm) { return sm == FP4_SCALE_NV_GIVEN || sm == FP4_SCALE_NV_4OVER6_GIVEN; }
 
 int scale_class(int sm) {
     if (sm == FP4_SCALE_E8M0_FLOOR || sm == FP4_SCALE_E8M0_CEIL) return SC_E8M0;
@@ -31,7 +36,7 @@ int check_params(int64_t rows, int64_t cols, const fp4_qparams* p, Layout* lay) 
     *lay = L_BAD;
     if (!p || rows <= 0 || cols <= 0) return FP4_ERR_INVALID_ARG;
     if (p->elem != FP4_ELEM_E2M1 && p->elem != FP4_ELEM_E4M3) return FP4_ERR_INVALID_ARG;
-    if (p->scale_mode < FP4_SCALE_E8M0_FLOOR || p->scale_mode > FP4_SCALE_F32) return FP4_ERR_INVALID_ARG;
+    if (p->scale_mode < FP4_SCALE_E8M0_FLOOR || p->scale_mode > FP4_SCALE_NV_4OVER6_GIVEN) return FP4_ERR_INVALID_ARG;
     if (p->round_mode != FP4_ROUND_RNE && p->round_mode != FP4_ROUND_SR) return FP4_ERR_INVALID_ARG;
     if (p->block_rows <= 0 || p->block_cols <= 0) return FP4_ERR_INVALID_ARG;
     if (rows % p->block_rows || cols % p->block_cols) return FP4_ERR_INVALID_ARG;
@@ -46,7 +51,7 @@ int check_params(int64_t rows, int64_t cols, const fp4_qparams* p, Layout* lay) 
     else return FP4_ERR_UNSUPPORTED;
     if (is_nv(p->scale_mode)) {
         if (p->elem != FP4_ELEM_E2M1 || *lay != L_SEG1D || bc != 16) return FP4_ERR_UNSUPPORTED;
-        if (p->scale_mode == FP4_SCALE_NV_4OVER6 && p->round_mode == FP4_ROUND_SR) return FP4_ERR_UNSUPPORTED;
+        if (is_4over6(p->scale_mode) && p->round_mode == FP4_ROUND_SR) return FP4_ERR_UNSUPPORTED;
     }
     if (*lay == L_SEG2D && scale_class(p->scale_mode) != SC_E8M0) return FP4_ERR_UNSUPPORTED;
     if ((*lay == L_ROW || *lay == L_TENSOR) && p->hadamard_n) return FP4_ERR_UNSUPPORTED;
@@ -61,7 +66,7 @@ int64_t scales_bytes(int64_t rows, int64_t cols, const fp4_qparams* p) {
     return scale_class(p->scale_mode) == SC_F32 ? 4 * n : n;
 }
 int64_t ws_bytes_needed(Layout lay, const fp4_qparams* p) {
-    return (is_nv(p->scale_mode) || lay == L_TENSOR) ? 256 : 0;
+    return ((is_nv(p->scale_mode) && !is_given(p->scale_mode)) || lay == L_TENSOR) ? 256 : 0;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_HIP; }
@@ -140,8 +145,9 @@ int fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int
             a.ws = ws;
             a.seed = p->seed;
             a.ceil_rule = p->scale_mode == FP4_SCALE_E8M0_CEIL;
-            a.four_six = p->scale_mode == FP4_SCALE_NV_4OVER6;
-            if (sc == SC_NV) {
+            a.four_six = is_4over6(p->scale_mode);
+            a.nv_given = is_given(p->scale_mode);
+            if (sc == SC_NV && !a.nv_given) {
                 if ((rc = hip_status(launch_zero_u32(ws, 1, s))) != FP4_OK) return rc;
                 rc = hip_status(launch_segment(a, x_dtype, p->hadamard_n, p->elem, sc, p->round_mode, 1,
                                                32, PASS_AMAX, s));
@@ -209,9 +215,10 @@ int fp4_quantize_colwise(const void* x, int32_t x_dtype, int64_t rows, int64_t c
         a.ws = ws;
         a.seed = p->seed;
         a.ceil_rule = p->scale_mode == FP4_SCALE_E8M0_CEIL;
-        a.four_six = p->scale_mode == FP4_SCALE_NV_4OVER6;
+        a.four_six = is_4over6(p->scale_mode);
+        a.nv_given = is_given(p->scale_mode);
         a.colwise = 1;
-        if (sc == SC_NV) {
+        if (sc == SC_NV && !a.nv_given) {
             if ((rc = hip_status(launch_zero_u32(ws, 1, s))) != FP4_OK) return rc;
             rc = hip_status(launch_segment(a, x_dtype, p->hadamard_n, p->elem, sc, p->round_mode, 1, 32, PASS_AMAX, s));
             if (rc != FP4_OK) return rc;

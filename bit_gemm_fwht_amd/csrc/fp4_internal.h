@@ -24,6 +24,7 @@ struct SegArgs {
     uint64_t seed;
     int ceil_rule;
     int four_six;
+    int nv_given;          // NV: g is read from tensor_scale (no amax pass)
     // column-wise view: rows x cols describe T = x^T, x is [cols, rows] with row pitch ldx
     int colwise;
 };

@@ -372,9 +372,14 @@ __global__ __launch_bounds__(kThreads) void k_segment(SegArgs a) {
                 if (valid) reinterpret_cast<uint16_t*>(a.scales)[seg] = (uint16_t)(s0 | (s1 << 8));
             }
         } else if constexpr (SC == SC_NV) {
-            const float amax_t = __uint_as_float(*a.ws);
-            const float g = amax_t > 0.0f ? amax_t / 2688.0f : 1.0f;
-            if (blockIdx.x == 0 && threadIdx.x == 0) *a.tensor_scale = g;
+            float g;
+            if (a.nv_given) {
+                g = *a.tensor_scale;  // the caller's (delayed) tensor scale
+            } else {
+                const float amax_t = __uint_as_float(*a.ws);
+                g = amax_t > 0.0f ? amax_t / 2688.0f : 1.0f;
+                if (blockIdx.x == 0 && threadIdx.x == 0) *a.tensor_scale = g;
+            }
             const float m0 = block_amax<16, 0>(v), m1 = block_amax<16, 16>(v);
             const uint32_t s0 = nv_block<RND, 0>(v, m0, g, a.four_six != 0, rw, out);
             const uint32_t s1 = nv_block<RND, 16>(v, m1, g, a.four_six != 0, rw, out);

@@ -20,6 +20,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_WORKSPACE, ERR_HIP, ERR
 DT_F32, DT_BF16 = 0, 1
 E2M1, E4M3 = 0, 1
 SCALE_E8M0_FLOOR, SCALE_E8M0_CEIL, SCALE_NV, SCALE_NV_4OVER6, SCALE_F32 = range(5)
+SCALE_NV_GIVEN, SCALE_NV_4OVER6_GIVEN = 5, 6  # NVFP4 with the caller's (delayed) tensor scale
+NV_MODES = (SCALE_NV, SCALE_NV_4OVER6, SCALE_NV_GIVEN, SCALE_NV_4OVER6_GIVEN)
 ROUND_RNE, ROUND_SR = 0, 1
 
 
@@ -148,20 +150,33 @@ def empty_qtensor(rows: int, cols: int, params: Params, device) -> QTensor:
     cb, sb, _ = buffer_sizes(rows, cols, params)
     codes = torch.empty(max(cb, 1), dtype=torch.uint8, device=device)
     scales = torch.empty(max(sb, 1), dtype=torch.uint8, device=device)
-    nv = params.scale_mode in (SCALE_NV, SCALE_NV_4OVER6)
+    nv = params.scale_mode in NV_MODES
     ts = torch.empty(1, dtype=torch.float32, device=device) if nv else None
     return QTensor(codes, scales, ts, rows, cols, params)
 
 
+def _set_given_scale(q: QTensor, params: Params, tensor_scale) -> None:
+    """The _GIVEN NVFP4 modes read g from the output's tensor-scale buffer."""
+    if params.scale_mode in (SCALE_NV_GIVEN, SCALE_NV_4OVER6_GIVEN):
+        if tensor_scale is None:
+            raise ValueError("the _GIVEN scale modes need tensor_scale (the fp32 g)")
+        if isinstance(tensor_scale, torch.Tensor):
+            q.tensor_scale.copy_(tensor_scale.reshape(1))
+        else:
+            q.tensor_scale.fill_(float(tensor_scale))
+
+
 def quantize(x: torch.Tensor, params: Params = MXFP4, out: QTensor | None = None,
-             workspace: torch.Tensor | None = None) -> QTensor:
-    """Quantize a 2-D float32 / bfloat16 CUDA tensor along its last axis."""
+             workspace: torch.Tensor | None = None, tensor_scale=None) -> QTensor:
+    """Quantize a 2-D float32 / bfloat16 CUDA tensor along its last axis. tensor_scale: g for the
+    _GIVEN NVFP4 modes (a float or a one-element device tensor)."""
     if x.dim() != 2 or not x.is_cuda:
         raise ValueError("x must be a 2-D CUDA tensor")
     if x.stride(1) != 1:
         raise ValueError("x must be contiguous along its last axis")
     rows, cols = x.shape
     q = out if out is not None else empty_qtensor(rows, cols, params, x.device)
+    _set_given_scale(q, params, tensor_scale)
     _, _, wb = buffer_sizes(rows, cols, params)
     if wb and workspace is None:
         workspace = torch.empty(wb, dtype=torch.uint8, device=x.device)
@@ -177,7 +192,7 @@ def quantize(x: torch.Tensor, params: Params = MXFP4, out: QTensor | None = None
 
 
 def quantize_colwise(x: torch.Tensor, params: Params = MXFP4, out: QTensor | None = None,
-                     workspace: torch.Tensor | None = None) -> QTensor:
+                     workspace: torch.Tensor | None = None, tensor_scale=None) -> QTensor:
     """Quantize x^T (shape [cols, rows]) along its last axis, i.e. x along its first axis, without
     forming the transpose. Returns the QTensor of the cols x rows tensor."""
     if x.dim() != 2 or not x.is_cuda:
@@ -186,6 +201,7 @@ def quantize_colwise(x: torch.Tensor, params: Params = MXFP4, out: QTensor | Non
         raise ValueError("x must be contiguous along its last axis")
     rows, cols = x.shape
     q = out if out is not None else empty_qtensor(cols, rows, params, x.device)
+    _set_given_scale(q, params, tensor_scale)
     _, _, wb = buffer_sizes(cols, rows, params)
     if wb and workspace is None:
         workspace = torch.empty(wb, dtype=torch.uint8, device=x.device)

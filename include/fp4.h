@@ -35,7 +35,8 @@
  *    nibble is the sign; E4M3 -> [rows, cols] bytes. Contiguous.
  *  - scales: row-major [rows/block_rows, cols/block_cols]; one byte per block (E8M0 code k+127,
  *    or an E4M3 code in the NVFP4 modes), or one fp32 per block in FP4_SCALE_F32. Contiguous.
- *  - tensor_scale: one fp32 (NVFP4 modes only), written by fp4_quantize, read by the others.
+ *  - tensor_scale: one fp32 (NVFP4 modes only), written by fp4_quantize (read by it in the _GIVEN
+ *    modes), read by the others.
  *  - The quantization axis is always the contiguous `cols` axis (K for GEMM operands).
  */
 #ifndef BGF_FP4_H
@@ -68,7 +69,12 @@ enum {
     FP4_SCALE_E8M0_CEIL = 1,  /* truncation-free: the smallest 2^k with maxval * 2^k >= amax */
     FP4_SCALE_NV = 2,         /* NVFP4: s = E4M3(amax_b / (6 g)), g = amax_tensor / (6 * 448) */
     FP4_SCALE_NV_4OVER6 = 3,  /* NVFP4, per block the better of the maps amax->6 and amax->4 */
-    FP4_SCALE_F32 = 4         /* fp32 S = amax / maxval (per tensor / per row / per group) */
+    FP4_SCALE_F32 = 4,        /* fp32 S = amax / maxval (per tensor / per row / per group) */
+    /* NVFP4 (and 4/6) with the tensor scale g GIVEN by the caller in *tensor_scale (an input):
+     * delayed scaling, e.g. g from an earlier step's amax, so the quantize is a single pass with no
+     * tensor amax; blocks whose amax exceeds 6 * 448 * g get the largest block scale and saturate */
+    FP4_SCALE_NV_GIVEN = 5,
+    FP4_SCALE_NV_4OVER6_GIVEN = 6
 };
 enum { FP4_ROUND_RNE = 0, FP4_ROUND_SR = 1 };
 

@@ -17,6 +17,8 @@ from . import build as _build
 
 E2M1, E4M3 = 0, 1
 SCALE_E8M0_FLOOR, SCALE_E8M0_CEIL, SCALE_NV, SCALE_NV_4OVER6, SCALE_F32 = 0, 1, 2, 3, 4
+SCALE_NV_GIVEN, SCALE_NV_4OVER6_GIVEN = 5, 6  # NVFP4 with the caller's tensor scale
+NV_MODES = (SCALE_NV, SCALE_NV_4OVER6, SCALE_NV_GIVEN, SCALE_NV_4OVER6_GIVEN)
 ROUND_RNE, ROUND_SR = 0, 1
 IN_F32, IN_BF16 = 0, 1
 
@@ -160,10 +162,11 @@ def scales_shape(rows, cols, block):
 
 
 def quantize(x, *, elem=E2M1, block=(1, 32), scale_mode=SCALE_E8M0_FLOOR, round_mode=ROUND_RNE,
-             hadamard_n=0, seed=0):
+             hadamard_n=0, seed=0, tensor_scale=None):
     """Quantize a 2-D array along its last (contiguous) axis.
 
-    x: float32 array, or uint16 array holding bf16 bit patterns.
+    x: float32 array, or uint16 array holding bf16 bit patterns. tensor_scale: the given g of the
+    SCALE_NV*_GIVEN modes.
     Returns (codes uint8, scales uint8 or float32, tensor_scale float32 or None)."""
     x = np.asarray(x)
     if x.ndim != 2:
@@ -177,11 +180,15 @@ def quantize(x, *, elem=E2M1, block=(1, 32), scale_mode=SCALE_E8M0_FLOOR, round_
     sdt = np.float32 if scale_mode == SCALE_F32 else np.uint8
     scales = np.zeros(scales_shape(rows, cols, block), dtype=sdt)
     ts = np.zeros(1, dtype=np.float32)
+    if scale_mode in (SCALE_NV_GIVEN, SCALE_NV_4OVER6_GIVEN):
+        if tensor_scale is None:
+            raise ValueError("the _GIVEN modes need tensor_scale")
+        ts[0] = np.float32(tensor_scale)
     rc = lib().orc_quantize(_ptr(xd), dt, rows, cols, elem, block[0], block[1], scale_mode,
                             round_mode, hadamard_n, seed, _ptr(codes), _ptr(scales), _ptr(ts))
     if rc:
         raise ValueError(f"orc_quantize rejected the arguments (code {rc})")
-    nv = scale_mode in (SCALE_NV, SCALE_NV_4OVER6)
+    nv = scale_mode in NV_MODES
     return codes, scales, (ts if nv else None)
 
 

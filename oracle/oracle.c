@@ -12,6 +12,13 @@
 #include <stdlib.h>
 #include <string.h>
 
+static int is_nv_mode(int m) {
+    return m == ORC_SCALE_NV || m == ORC_SCALE_NV_4OVER6 || m == ORC_SCALE_NV_GIVEN ||
+           m == ORC_SCALE_NV_4OVER6_GIVEN;
+}
+static int is_4over6_mode(int m) { return m == ORC_SCALE_NV_4OVER6 || m == ORC_SCALE_NV_4OVER6_GIVEN; }
+static int is_given_mode(int m) { return m == ORC_SCALE_NV_GIVEN || m == ORC_SCALE_NV_4OVER6_GIVEN; }
+
 /* ------------------------------------------------------------------------------------------------
  * Number formats
  * ----------------------------------------------------------------------------------------------*/
@@ -245,12 +252,12 @@ static int check_layout(int64_t rows, int64_t cols, int elem, int br, int bc, in
     if (rows % br || cols % bc) return -2;
     if (elem != ORC_ELEM_E2M1 && elem != ORC_ELEM_E4M3) return -3;
     if (elem == ORC_ELEM_E2M1 && (cols & 1)) return -4;
-    if (scale_mode < 0 || scale_mode > 4) return -5;
+    if (scale_mode < 0 || scale_mode > 6) return -5;
     if (round_mode != ORC_ROUND_RNE && round_mode != ORC_ROUND_SR) return -6;
     if (hadamard_n && (!is_pow2(hadamard_n) || hadamard_n < 2 || cols % hadamard_n)) return -7;
-    if (scale_mode == ORC_SCALE_NV || scale_mode == ORC_SCALE_NV_4OVER6) {
+    if (is_nv_mode(scale_mode)) {
         if (elem != ORC_ELEM_E2M1 || br != 1 || !is_pow2(bc) || bc > 64) return -8;
-        if (scale_mode == ORC_SCALE_NV_4OVER6 && round_mode == ORC_ROUND_SR) return -9;
+        if (is_4over6_mode(scale_mode) && round_mode == ORC_ROUND_SR) return -9;
     }
     return 0;
 }
@@ -333,9 +340,17 @@ int orc_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int ele
     if (!xf) return -100;
     if (hadamard_n) orc_fwht(xf, n, hadamard_n);
 
-    const int nv = (scale_mode == ORC_SCALE_NV || scale_mode == ORC_SCALE_NV_4OVER6);
+    const int nv = is_nv_mode(scale_mode);
     float g = 1.0f;
-    if (nv) {
+    if (is_given_mode(scale_mode)) {
+        /* delayed scaling: the caller's g; blocks whose amax exceeds 6 * 448 * g get the largest
+         * block scale and their elements saturate */
+        if (!tensor_scale) {
+            free(xf);
+            return -10;
+        }
+        g = *tensor_scale;
+    } else if (nv) {
         /* fp32 tensor scale g = amax_t / (6 * 448), so that the block scales use the E4M3 range */
         float amax_t = 0.0f;
         for (int64_t i = 0; i < n; ++i) amax_t = fmaxf(amax_t, fabsf(xf[i]));
@@ -368,7 +383,7 @@ int orc_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int ele
                 uint8_t s6 = nv_candidate(amax, g, 6.0f, &d6);
                 uint8_t s = s6;
                 d = d6;
-                if (scale_mode == ORC_SCALE_NV_4OVER6) {
+                if (is_4over6_mode(scale_mode)) {
                     /* [4over6] methodology: a second candidate maps the block max to 4 instead of
                      * 6; keep the one with the lower block error (strictly lower, else 6). */
                     float d4;
@@ -433,7 +448,7 @@ int orc_operand_f64(const uint8_t* codes, const void* scales, const float* tenso
     int rc = check_layout(rows, K, elem, block_rows, block_cols, scale_mode, ORC_ROUND_RNE, 0);
     if (rc) return rc;
     const int64_t nbc = K / block_cols;
-    const int nv = (scale_mode == ORC_SCALE_NV || scale_mode == ORC_SCALE_NV_4OVER6);
+    const int nv = is_nv_mode(scale_mode);
     if (!nv || with_nv_exact) {
         for (int64_t r = 0; r < rows; ++r)
             for (int64_t k = 0; k < K; ++k) {

@@ -40,6 +40,11 @@ extern "C" {
 #define ORC_SCALE_NV 2          /* E4M3 block scale x fp32 tensor scale (NVFP4) */
 #define ORC_SCALE_NV_4OVER6 3   /* NVFP4 with the 4/6 choice per block */
 #define ORC_SCALE_F32 4         /* fp32 scale S = amax / maxval */
+/* NVFP4 with a tensor scale g given by the caller (delayed scaling: g from an earlier amax, the
+ * moving-average scale the Quartet notes' open questions point to) instead of this tensor's amax;
+ * tensor_scale is then an input */
+#define ORC_SCALE_NV_GIVEN 5
+#define ORC_SCALE_NV_4OVER6_GIVEN 6
 /* rounding */
 #define ORC_ROUND_RNE 0
 #define ORC_ROUND_SR 1
@@ -73,7 +78,7 @@ int orc_e8m0_scale_exp(float amax, int elem, int rule);   /* returns k (E8M0 cod
  * codes: E2M1 -> [rows, cols/2] bytes, element 2j in the low nibble of byte j;
  *        E4M3 -> [rows, cols] bytes.
  * scales: [rows/block_rows, cols/block_cols]; u8 E8M0 / E4M3 codes, or fp32 for ORC_SCALE_F32.
- * tensor_scale: NV modes only, receives g (may be NULL otherwise).
+ * tensor_scale: NV modes only, receives g (may be NULL otherwise); the _GIVEN modes read g from it.
  * Returns 0, or a negative number for an argument it does not accept. */
 int orc_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int elem,
                  int block_rows, int block_cols, int scale_mode, int round_mode, int hadamard_n,

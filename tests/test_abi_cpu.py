@@ -181,3 +181,16 @@ def test_quantize_colwise_validation_without_device(fp4):
     assert _quant_cw(fp4, P(fp4), ldx=66) == E.ERR_ALIGNMENT
     assert _quant_cw(fp4, P(fp4), ldx=32) == E.ERR_INVALID_ARG            # ldx < cols
     assert _quant_cw(fp4, P(fp4), codes=0x1000) == E.ERR_INVALID_ARG      # aliasing
+
+
+def test_nv_given_validation_without_device(fp4):
+    """The _GIVEN NVFP4 modes need no workspace (no amax pass) but do need tensor_scale."""
+    E = fp4
+    L = fp4.lib()
+    p = P(fp4, scale_mode=5, block_cols=16)
+    assert L.fp4_workspace_bytes(64, 256, ctypes.byref(p)) == 0
+    assert L.fp4_workspace_bytes(64, 256, ctypes.byref(P(fp4, scale_mode=2, block_cols=16))) == 256
+    assert _quant(fp4, p) == E.ERR_INVALID_ARG                          # no tensor_scale
+    assert _quant(fp4, P(fp4, scale_mode=6, block_cols=32), ts=0x4000) == E.ERR_UNSUPPORTED
+    assert _quant(fp4, P(fp4, scale_mode=6, block_cols=16, round_mode=1), ts=0x4000) == E.ERR_UNSUPPORTED
+    assert _quant(fp4, P(fp4, scale_mode=7, block_cols=16), ts=0x4000) == E.ERR_INVALID_ARG

@@ -224,7 +224,7 @@ def _gemm_tol(ref, sabs, a64, b64, im, inn, params_a, K, c_dtype):
     zero), so each instruction may lose up to 128 * 2^(e - 13), e = floor(log2 max |a_k b_k|) over
     its 128-wide K slice."""
     tol = 1e-5 * sabs
-    if params_a.elem == E4M3 or params_a.scale_mode in (NV, NV46):
+    if params_a.elem == E4M3 or params_a.scale_mode in fp4.NV_MODES:
         pm = _slice_max(a64, b64, im, inn, K)
         e = np.floor(np.log2(np.where(pm > 0, pm, 1.0)))
         tol = tol + np.where(pm > 0, 128.0 * 2.0 ** (e - 13), 0.0).sum(axis=-1)
@@ -426,3 +426,52 @@ def test_weight_gradient_gemm_colwise(orc):
     ref, sabs = orc.gemm_f64(a64, b64)
     err = np.abs(dw.cpu().numpy().astype(np.float64) - ref)
     assert np.all(err <= 1e-5 * sabs + 1e-30)
+
+
+NVG, NV46G = fp4.SCALE_NV_GIVEN, fp4.SCALE_NV_4OVER6_GIVEN
+
+
+@pytest.mark.parametrize("mode", [NVG, NV46G])
+@pytest.mark.parametrize("gfac", [1.0, 0.25, 3.0])
+@pytest.mark.parametrize("hn,rnd", [(0, RNE), (128, RNE), (0, SR)])
+def test_nvfp4_given_tensor_scale_parity(orc, mode, gfac, hn, rnd):
+    """Delayed NVFP4 scaling: codes and scales bit-exact against the oracle for the caller's g
+    (the tensor's own amax-derived g times gfac: below 1 some blocks saturate), row-wise and
+    column-wise, and the GEMM on such operands within the bound."""
+    if mode == NV46G and rnd == SR:
+        pytest.skip("SR is not combined with 4/6")
+    rng = np.random.default_rng(int(gfac * 10) + hn)
+    x = (rng.laplace(size=(256, 256)) * 2).astype(np.float32)
+    xb = wl.f32_to_bf16_bits(x)
+    g0 = float(np.abs(wl.bf16_bits_to_f32(xb)).max()) / 2688.0
+    g = float(np.float32(g0 * gfac))
+    params = P(block=(1, 16), scale_mode=mode, round_mode=rnd, hadamard_n=hn, seed=5)
+    q = fp4.quantize(_to_dev(xb), params, tensor_scale=g)
+    torch.cuda.synchronize()
+    oc, os_, ots = orc.quantize(xb, block=(1, 16), scale_mode=mode, round_mode=rnd, hadamard_n=hn,
+                                seed=5, tensor_scale=g)
+    assert np.array_equal(q.codes.cpu().numpy(), oc.reshape(-1))
+    assert np.array_equal(q.scales.cpu().numpy(), os_.reshape(-1))
+    assert q.tensor_scale.cpu().numpy()[0] == np.float32(g)
+    qt = fp4.quantize_colwise(_to_dev(xb), params, tensor_scale=g)
+    torch.cuda.synchronize()
+    oct_, ost, _ = orc.quantize(np.ascontiguousarray(xb.T), block=(1, 16), scale_mode=mode,
+                                round_mode=rnd, hadamard_n=hn, seed=5, tensor_scale=g)
+    assert np.array_equal(qt.codes.cpu().numpy(), oct_.reshape(-1))
+    assert np.array_equal(qt.scales.cpu().numpy(), ost.reshape(-1))
+    if rnd == RNE:
+        w = (rng.standard_normal((160, 256)) * 0.02).astype(np.float32)
+        pw = P(block=(1, 16), scale_mode=mode, hadamard_n=hn)
+        gw = float(np.abs(w).max()) / 2688.0 * 0.5
+        cb, sb, tb = orc.quantize(w, block=(1, 16), scale_mode=mode, hadamard_n=hn, tensor_scale=gw)
+        qb = fp4.upload_qtensor(cb, sb, tb, 160, 256, pw, DEV)
+        qa = fp4.upload_qtensor(oc, os_, ots, 256, 256, params, DEV)
+        c = fp4.gemm(qa, qb, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        a64 = orc.operand_f64(oc, os_, ots, 256, 256, block=(1, 16), scale_mode=mode)
+        b64 = orc.operand_f64(cb, sb, tb, 160, 256, block=(1, 16), scale_mode=mode)
+        ref, sabs = orc.gemm_f64(a64, b64)
+        im, inn = np.repeat(np.arange(256), 160), np.tile(np.arange(160), 256)
+        tol = _gemm_tol(ref.reshape(-1), sabs.reshape(-1), a64, b64, im, inn, params, 256,
+                        torch.float32).reshape(256, 160)
+        assert np.all(np.abs(c.cpu().numpy() - ref) <= tol)

@@ -562,3 +562,32 @@ def test_gemm_reference_against_numpy(orc):
     ns = np.array([3, 0, 255])
     c2, s2 = orc.gemm_f64_sampled(A, B, ms, ns)
     assert np.array_equal(c2, c[ms, ns]) and np.array_equal(s2, s[ms, ns])
+
+
+def test_nvfp4_given_tensor_scale(orc):
+    """Delayed NVFP4 scaling (the caller's tensor scale g): with g equal to the tensor's own
+    amax / 2688 it reduces to plain NVFP4 (and 4/6), byte for byte; with g far below that every
+    block scale saturates to the largest E4M3 value (code 0x7E) and the block's largest elements to
+    +-6; 4/6 is never worse than its 6-only counterpart per block."""
+    rng = np.random.default_rng(17)
+    x = (rng.laplace(size=(16, 128)) * 3).astype(np.float32)
+    for plain, given in ((orc.SCALE_NV, orc.SCALE_NV_GIVEN), (orc.SCALE_NV_4OVER6, orc.SCALE_NV_4OVER6_GIVEN)):
+        c0, s0, t0 = orc.quantize(x, block=(1, 16), scale_mode=plain)
+        c1, s1, t1 = orc.quantize(x, block=(1, 16), scale_mode=given, tensor_scale=t0[0])
+        assert np.array_equal(c0, c1) and np.array_equal(s0, s1) and t1[0] == t0[0]
+    amax_b = np.abs(x).reshape(16, 8, 16).max(axis=-1)
+    g_small = float(amax_b.min()) / (6 * 448 * 100)
+    c, s, _ = orc.quantize(x, block=(1, 16), scale_mode=orc.SCALE_NV_GIVEN, tensor_scale=g_small)
+    assert np.all(s == 0x7E)
+    mag = np.stack([c & 0xF, c >> 4], axis=-1).reshape(16, 8, 16) & 7
+    arg = np.abs(x).reshape(16, 8, 16).argmax(axis=-1)
+    assert np.all(np.take_along_axis(mag, arg[..., None], -1) == 7)
+    g = float(np.abs(x).max()) / 2688 * 0.37
+    c6, s6, _ = orc.quantize(x, block=(1, 16), scale_mode=orc.SCALE_NV_GIVEN, tensor_scale=g)
+    c46, s46, _ = orc.quantize(x, block=(1, 16), scale_mode=orc.SCALE_NV_4OVER6_GIVEN, tensor_scale=g)
+    gt = np.array([g], np.float32)
+    y6 = orc.dequantize(c6, s6, gt, 16, 128, block=(1, 16), scale_mode=orc.SCALE_NV_GIVEN)
+    y46 = orc.dequantize(c46, s46, gt, 16, 128, block=(1, 16), scale_mode=orc.SCALE_NV_4OVER6_GIVEN)
+    e6 = ((y6.astype(np.float64) - x) ** 2).reshape(16, 8, 16).sum(-1)
+    e46 = ((y46.astype(np.float64) - x) ** 2).reshape(16, 8, 16).sum(-1)
+    assert np.all(e46 <= e6 * (1 + 1e-6) + 1e-30)
