@@ -199,20 +199,27 @@ __device__ __forceinline__ uint32_t nv_candidate(float amax, float g, float M, f
     return s;
 }
 
-// block SSE of RNE encoding with scale d (fixed pairwise tree over the 16 terms)
+// RNE codes of the 16-element block at OFF with scale d (r = its reciprocal), packed as the encode
+// does (two words, element j in nibble j % 8 of word j / 8), and the block's SSE of the decoded
+// values in the fixed pairwise tree over the 16 squared errors RN(x - RN(q d))^2.
 template <int OFF>
-__device__ __forceinline__ float sse16(const float (&v)[32], float d) {
-    const float r = scale_recip(d);
+__device__ __forceinline__ float nv_codes_sse(const float (&v)[32], float d, float r, uint32_t (&code)[2]) {
     float t[16];
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-        const float a = v[OFF + i] * r, b = v[OFF + i + 1] * r;
-        const uint32_t q = cvt_fp4x2<0>(0u, a, b, 1.0f);
-        const v2f dq = fp4x2_to_f32<0>(q);
-        const float e0 = v[OFF + i] - dq[0] * d;
-        const float e1 = v[OFF + i + 1] - dq[1] * d;
-        t[i] = e0 * e0;
-        t[i + 1] = e1 * e1;
+    for (int w = 0; w < 2; ++w) {
+        const int b = OFF + 8 * w;
+        uint32_t c = cvt_fp4x2<0>(0u, v[b] * r, v[b + 1] * r, 1.0f);
+        c = cvt_fp4x2<1>(c, v[b + 2] * r, v[b + 3] * r, 1.0f);
+        c = cvt_fp4x2<2>(c, v[b + 4] * r, v[b + 5] * r, 1.0f);
+        c = cvt_fp4x2<3>(c, v[b + 6] * r, v[b + 7] * r, 1.0f);
+        code[w] = c;
+        const v2f q0 = fp4x2_to_f32<0>(c), q1 = fp4x2_to_f32<1>(c), q2 = fp4x2_to_f32<2>(c), q3 = fp4x2_to_f32<3>(c);
+        const float dq[8] = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float e = v[b + j] - dq[j] * d;
+            t[8 * w + j] = e * e;
+        }
     }
 #pragma unroll
     for (int w = 16; w > 1; w >>= 1)
@@ -221,19 +228,24 @@ __device__ __forceinline__ float sse16(const float (&v)[32], float d) {
     return t[0];
 }
 
-// NVFP4 path for one 16-element block: returns the E4M3 scale code.
+// NVFP4 path for one 16-element block: returns the E4M3 scale code. With four_six (RNE only) both
+// candidates are encoded once; the SSE comparison picks one and its codes are kept as they are.
 template <int RND, int OFF>
 __device__ __forceinline__ uint32_t nv_block(float (&v)[32], float amax, float g, bool four_six,
                                              const uint32_t (&rw)[16], uint32_t (&out)[8]) {
     float d;
     uint32_t s = nv_candidate(amax, g, 6.0f, d);
-    if (four_six) {
-        float d4;
-        const uint32_t s4 = nv_candidate(amax, g, 4.0f, d4);
-        const float e6 = sse16<OFF>(v, d), e4 = sse16<OFF>(v, d4);
-        if (e4 < e6) {
-            s = s4;
-            d = d4;
+    if constexpr (RND == RND_RNE) {
+        if (four_six) {
+            float d4;
+            const uint32_t s4 = nv_candidate(amax, g, 4.0f, d4);
+            uint32_t c6[2], c4[2];
+            const float e6 = nv_codes_sse<OFF>(v, d, scale_recip(d), c6);
+            const float e4 = nv_codes_sse<OFF>(v, d4, scale_recip(d4), c4);
+            const bool four = e4 < e6;
+            out[OFF / 8] = four ? c4[0] : c6[0];
+            out[OFF / 8 + 1] = four ? c4[1] : c6[1];
+            return four ? s4 : s;
         }
     }
     encode_block<ELEM_E2M1, RND, 16, OFF>(v, false, 1.0f, scale_recip(d), 448.0f, rw, out);
