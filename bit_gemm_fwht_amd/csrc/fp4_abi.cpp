@@ -355,7 +355,8 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
         int b2d;
         const int kind = gemm_kind(A, B, &b2d);
         if (kind < 0) return FP4_ERR_UNSUPPORTED;
-        // fused output quantization: MX groups of 32 along N, E8M0 floor / ceil, no rotation
+        // fused output quantization: MX groups of 32 along N, E8M0 floor / ceil, optional rotation
+        // of C along N (n <= 128) before it
         const bool fq = out_q != nullptr;
         if (fq != (C_q != nullptr)) return FP4_ERR_INVALID_ARG;
         if (fq) {
@@ -364,8 +365,9 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
             if (out_q->block_rows != 1 || out_q->block_cols != 32) return FP4_ERR_UNSUPPORTED;
             if (out_q->scale_mode != FP4_SCALE_E8M0_FLOOR && out_q->scale_mode != FP4_SCALE_E8M0_CEIL)
                 return FP4_ERR_UNSUPPORTED;
-            if (out_q->hadamard_n != 0) return FP4_ERR_UNSUPPORTED;
-            if (N % 32) return FP4_ERR_INVALID_ARG;
+            if (!valid_hn(out_q->hadamard_n)) return FP4_ERR_INVALID_ARG;
+            if (out_q->hadamard_n > 128) return FP4_ERR_UNSUPPORTED;
+            if (N % 32 || (out_q->hadamard_n && N % out_q->hadamard_n)) return FP4_ERR_INVALID_ARG;
             if (!C_q->codes || !C_q->scales) return FP4_ERR_INVALID_ARG;
             if (!aligned(C_q->codes, 16)) return FP4_ERR_ALIGNMENT;
         }
@@ -402,6 +404,7 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
             g.q_ceil = out_q->scale_mode == FP4_SCALE_E8M0_CEIL;
             g.q_round = out_q->round_mode == FP4_ROUND_SR ? RND_SR : RND_RNE;
             g.q_seed = out_q->seed;
+            g.q_hn = out_q->hadamard_n;
             // describe what was written
             C_q->rows = M;
             C_q->cols = N;

@@ -75,7 +75,7 @@ struct GemmArgs {
     // fused output quantization along N (MX groups of 32)
     uint8_t* qcodes;
     uint8_t* qscales;
-    int q_elem, q_ceil, q_round;
+    int q_elem, q_ceil, q_round, q_hn;  // q_hn: rotation of C along N before the quantize (0 = none)
     uint64_t q_seed;
     // NV operands re-expressed as MXFP8 (workspace)
     uint8_t* a8;

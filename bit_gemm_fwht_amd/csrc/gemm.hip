@@ -45,60 +45,22 @@ struct Cfg {
 };
 
 // ---------------------------------------------------------------------------------------------
-// Fused output quantization ("online quantization" of the GEMM output in the QuTLASS kernel list of
-// the Quartet lecture notes): C, as the fp32 values the plain output path would store (accumulator
-// times the NVFP4 tensor-scale product), quantized along N in MX groups of 32 with the rules of the
-// quantize kernels: E8M0 floor or ceil scale from the group amax, E2M1 or E4M3 elements, round to
-// nearest even (hardware convert) or stochastic rounding keyed by the row-major index m * N + n of
-// C. Codes are [M, N/2] (E2M1) or [M, N] (E4M3) bytes, scales [M, N/32].
+// Fused output quantization ("online quantization" of the GEMM output in the QuTLASS kernel list
+// of the Quartet lecture notes), in both kernels' epilogues: C, as the fp32 values the plain output
+// path would store (accumulator times the NVFP4 tensor-scale product), optionally rotated along N
+// by the blockwise H_n / sqrt(n) (n <= 128), quantized along N in MX groups of 32 with the rules of
+// the quantize kernels: E8M0 floor or ceil scale from the group amax, E2M1 or E4M3 elements, round
+// to nearest even or stochastic rounding keyed by the row-major index m * N + n of C. Codes are
+// [M, N/2] (E2M1) or [M, N] (E4M3) bytes, scales [M, N/32]. The C tile is staged in LDS so that
+// one lane holds one group and the groups of a row sit in consecutive lanes.
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ int outq_exp(const GemmArgs& g, float amax) {
-    return g.q_elem == ELEM_E2M1 ? e8m0_exp<2, 0x400000u>(amax, g.q_ceil != 0)
-                                 : e8m0_exp<8, 0x600000u>(amax, g.q_ceil != 0);
-}
-
-// Codes of v[i] = C[m][n0 + i], i = 0..3 (n0 % 4 == 0), under the scale 2^k; idx0 = m * N + n0.
-// E2M1: element i in nibble i of the low 16 bits; E4M3: element i in byte i.
-__device__ __forceinline__ uint32_t outq_encode4(const GemmArgs& g, float (&v)[4], int k, int64_t idx0) {
-    if (k == -127) {
-        // 2^-127 is not a normal fp32: divide by 2^-126 after doubling (exact for such tiny values)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = v[i] * 2.0f;
-        k = -126;
-    }
-    const float scale = pow2f(k);
-    if (g.q_round == RND_RNE) {
-        if (g.q_elem == ELEM_E2M1) {
-            uint32_t r = cvt_fp4x2<0>(0u, v[0], v[1], scale);
-            return cvt_fp4x2<1>(r, v[2], v[3], scale);
-        }
-        const float cl = 448.0f * scale;  // saturate before the non-saturating convert
-        uint32_t r = cvt_fp8x2<false>(0u, __builtin_amdgcn_fmed3f(v[0], -cl, cl), __builtin_amdgcn_fmed3f(v[1], -cl, cl), scale);
-        return cvt_fp8x2<true>(r, __builtin_amdgcn_fmed3f(v[2], -cl, cl), __builtin_amdgcn_fmed3f(v[3], -cl, cl), scale);
-    }
-    // SR: one Philox call covers elements 8 (idx0 / 8) .. + 7; element j of it takes half j % 2 of
-    // word j / 2
-    const float rcp = __builtin_amdgcn_ldexpf(1.0f, -k);
-    const uint64_t ctr = (uint64_t)idx0 >> 3;
-    uint32_t c0 = (uint32_t)ctr, c1 = (uint32_t)(ctr >> 32), c2 = 0u, c3 = 0u;
-    philox4x32_10(c0, c1, c2, c3, (uint32_t)g.q_seed, (uint32_t)(g.q_seed >> 32));
-    const bool hi = (idx0 & 7) != 0;  // elements 4..7 of the call: words 2 and 3
-    const uint32_t wa = hi ? c2 : c0, wb = hi ? c3 : c1;
-    const uint32_t u[4] = {wa & 0xFFFFu, wa >> 16, wb & 0xFFFFu, wb >> 16};
-    uint32_t r = 0u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float x = v[i] * rcp;
-        r |= g.q_elem == ELEM_E2M1 ? e2m1_sr(x, u[i]) << (4 * i) : e4m3_sr(x, u[i]) << (8 * i);
-    }
-    return r;
-}
-
 template <bool FP8, bool B2D, int OUT, bool NVG, bool FQ>
 __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
     using C = Cfg<FP8>;
-    __shared__ __attribute__((aligned(16))) uint8_t sA[BM * C::LD];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[BN * C::LD];
+    // operand slabs; the fused output quantize reuses them to stage 32 rows of C at a time
+    __shared__ __attribute__((aligned(16))) uint8_t sAB[(BM + BN) * C::LD];
+    uint8_t* const sA = sAB;
+    uint8_t* const sB = sAB + BM * C::LD;
     __shared__ uint32_t sSA[BM], sSB[BN];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -194,40 +156,63 @@ __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
     float gscale = 1.0f;
     if constexpr (NVG) gscale = (*g.ga) * (*g.gb);
     if constexpr (FQ) {
-        // a 32-column group of row m is tiles in = 2 gq, 2 gq + 1 of lanes fr, fr + 16, fr + 32,
-        // fr + 48: 8 values per lane, amax over the four lanes
+        // fused output quantization (the rules of the big kernel's epilogue): four rounds of 32
+        // rows; the two waves holding a round's rows stage their fp32 values in LDS, then one
+        // thread per 32-column group (the four groups of a row in consecutive lanes) reads its
+        // group back, rotates it along N if asked and quantizes it
+        constexpr int EQ = 528;  // staged row pitch: 128 fp32 + 16 bytes of padding
+        static_assert(32 * EQ <= (BM + BN) * C::LD, "staging exceeds the operand slabs");
+        for (int rr = 0; rr < 4; ++rr) {
+            __syncthreads();  // the slabs are free (main loop / previous round done)
+            if (wm == (rr >> 1)) {  // wave-uniform
 #pragma unroll
-        for (int im = 0; im < 4; ++im)
+                for (int im = 0; im < 4; ++im) {
+                    if ((im >> 1) != (rr & 1)) continue;
+                    const int row = 16 * (im & 1) + fr;
 #pragma unroll
-            for (int gq = 0; gq < 2; ++gq) {
-                const int64_t m = m0 + wm * 64 + 16 * im + fr;
-                const int64_t nb = n0 + wn * 64 + 32 * gq;
-                float v0[4], v1[4];
-                float amax = 0.0f;
+                    for (int in = 0; in < 4; ++in) {
+                        f32x4 v;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v0[i] = NVG ? acc[2 * gq][im][i] * gscale : acc[2 * gq][im][i];
-                    v1[i] = NVG ? acc[2 * gq + 1][im][i] * gscale : acc[2 * gq + 1][im][i];
-                    amax = fmaxf(amax, fmaxf(fabsf(v0[i]), fabsf(v1[i])));
-                }
-                amax = fmaxf(amax, __shfl_xor(amax, 16));
-                amax = fmaxf(amax, __shfl_xor(amax, 32));
-                const int k = outq_exp(g, amax);
-                const uint32_t p0 = outq_encode4(g, v0, k, m * g.N + nb + 4 * fg);
-                const uint32_t p1 = outq_encode4(g, v1, k, m * g.N + nb + 16 + 4 * fg);
-                if (m < g.M && nb < g.N) {
-                    if (g.q_elem == ELEM_E2M1) {
-                        uint8_t* q = g.qcodes + m * (g.N / 2) + nb / 2;
-                        *reinterpret_cast<uint16_t*>(q + 2 * fg) = (uint16_t)p0;
-                        *reinterpret_cast<uint16_t*>(q + 8 + 2 * fg) = (uint16_t)p1;
-                    } else {
-                        uint8_t* q = g.qcodes + m * g.N + nb;
-                        *reinterpret_cast<uint32_t*>(q + 4 * fg) = p0;
-                        *reinterpret_cast<uint32_t*>(q + 16 + 4 * fg) = p1;
+                        for (int i = 0; i < 4; ++i) v[i] = NVG ? acc[in][im][i] * gscale : acc[in][im][i];
+                        *reinterpret_cast<f32x4*>(sAB + row * EQ + 4 * (wn * 64 + 16 * in + 4 * fg)) = v;
                     }
-                    if (fg == 0) g.qscales[m * (g.N / 32) + nb / 32] = (uint8_t)(k + 127);
                 }
             }
+            __syncthreads();
+            if (tid < 128) {  // waves 0 and 1, every lane
+                const int r = tid >> 2, j = tid & 3;
+                const int64_t m = m0 + 32 * rr + r, nb = n0 + 32 * j;
+                float v[32];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(sAB + r * EQ + 4 * (32 * j + 4 * c));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[4 * c + i] = x[i];
+                }
+                fwht_groups(v, g.q_hn);
+                uint32_t rw[16], out[8];
+                const float amax = block_amax<32, 0>(v);
+                uint32_t sbyte;
+                if (g.q_round == RND_SR) {
+                    philox_segment(g.q_seed, (uint64_t)(m * g.N + nb), rw);
+                    sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, rw, out)
+                                                  : e8m0_block<ELEM_E4M3, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, rw, out);
+                } else {
+                    sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_RNE, 32, 0>(v, amax, g.q_ceil != 0, rw, out)
+                                                  : e8m0_block<ELEM_E4M3, RND_RNE, 32, 0>(v, amax, g.q_ceil != 0, rw, out);
+                }
+                if (m < g.M && nb < g.N) {
+                    if (g.q_elem == ELEM_E2M1) {
+                        *reinterpret_cast<u32x4*>(g.qcodes + m * (g.N / 2) + nb / 2) = (u32x4){out[0], out[1], out[2], out[3]};
+                    } else {
+                        u32x4* d = reinterpret_cast<u32x4*>(g.qcodes + m * g.N + nb);
+                        d[0] = (u32x4){out[0], out[1], out[2], out[3]};
+                        d[1] = (u32x4){out[4], out[5], out[6], out[7]};
+                    }
+                    g.qscales[m * (g.N / 32) + nb / 32] = (uint8_t)sbyte;
+                }
+            }
+        }
         if (!g.c) return;
     }
 #pragma unroll
@@ -550,33 +535,34 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
     const int64_t Mx = g.M + opaque_zero, Nx = g.N + opaque_zero;
     if constexpr (FQ) {
         // fused output quantization, in two passes of 128 columns: the fp32 values (as an fp32 C
-        // would hold them) are staged in LDS, [256 rows][128] per pass (pass p holds tile in = p
-        // of every wave: staged column 32 wn + j is column 64 wn + 32 p + j of the tile), then one
-        // thread per 32-column group reads its group back and quantizes it with the rules of the
-        // quantize kernels
-        static_assert(C::WTN == 2, "one staged pass per wave tile column");
-        for (int p = 0; p < C::WTN; ++p) {
+        // would hold them) are staged in LDS, [256 rows][128] per pass (pass p holds tile columns
+        // [128 p, 128 p + 128), written by the four waves with wn / 2 = p), then one thread per
+        // 32-column group reads its group back, rotates it along N if asked (the four groups of a
+        // row are in consecutive lanes) and quantizes it with the rules of the quantize kernels
+        static_assert(C::WTN == 2 && C::NTH == 512, "two staged passes of 128 columns");
+        for (int p = 0; p < 2; ++p) {
             barrier_only();  // every wave is done with the stage buffers / the last pass
+            if ((wn >> 1) == p) {  // wave-uniform
 #pragma unroll
-            for (int im = 0; im < C::WTM; ++im) {
-                const int row = wm * 128 + 32 * im + fr;
+                for (int in = 0; in < C::WTN; ++in)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    f32x4 v;
+                    for (int im = 0; im < C::WTM; ++im) {
+                        const int row = wm * 128 + 32 * im + fr;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float a = p == 0 ? acc[0][im][4 * q + i] : acc[C::WTN - 1][im][4 * q + i];
-                        v[i] = NVG ? a * gscale : a;
+                        for (int q = 0; q < 4; ++q) {
+                            f32x4 v;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) v[i] = NVG ? acc[in][im][4 * q + i] * gscale : acc[in][im][4 * q + i];
+                            *reinterpret_cast<f32x4*>(smem + row * EP + 4 * (64 * (wn & 1) + 32 * in + 8 * q + 4 * fg)) = v;
+                        }
                     }
-                    *reinterpret_cast<f32x4*>(smem + row * EP + 4 * (wn * 32 + 8 * q + 4 * fg)) = v;
-                }
             }
             wait_lgkm0();
             barrier_only();
 #pragma unroll 1
-            for (int t = tid; t < 256 * 4; t += C::NTH) {
+            for (int t = tid; t < 256 * 4; t += C::NTH) {  // two sweeps, every lane in both
                 const int r = t >> 2, j = t & 3;  // row, staged group
-                const int64_t m = me0 + r, nb = ne0 + 64 * j + 32 * p;
+                const int64_t m = me0 + r, nb = ne0 + 128 * p + 32 * j;
                 float v[32];
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
@@ -584,6 +570,7 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) v[4 * c + i] = x[i];
                 }
+                fwht_groups(v, g.q_hn);
                 uint32_t rw[16], out[8];
                 const float amax = block_amax<32, 0>(v);
                 uint32_t sbyte;
@@ -608,13 +595,13 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
             }
             if (g.c) {
                 // C from the same staged values: 16-byte output pieces, staged column c of a row
-                // is tile column 64 (c / 32) + 32 p + c % 32
+                // is tile column 128 p + c
                 constexpr int ESZ = OUT == DT_F32 ? 4 : 2, EPC = 16 / ESZ, PPR = 128 / EPC;
                 const bool vec_ok = ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) && ((ldc * ESZ) % 16 == 0);
 #pragma unroll 1
                 for (int t = tid; t < 256 * PPR; t += C::NTH) {
                     const int r = t / PPR, c = (t % PPR) * EPC;
-                    const int64_t m = me0 + r, n = ne0 + 64 * (c >> 5) + 32 * p + (c & 31);
+                    const int64_t m = me0 + r, n = ne0 + 128 * p + c;
                     if (m >= Mx) continue;
                     const float* src = reinterpret_cast<const float*>(smem + r * EP) + c;
                     u32x4 val;

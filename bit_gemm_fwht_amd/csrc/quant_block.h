@@ -35,6 +35,43 @@ __device__ __forceinline__ uint32_t sr_u16(const uint32_t (&w)[16], int j) {
     return (j & 1) ? (word >> 16) : (word & 0xFFFFu);
 }
 
+// Blockwise H_n / sqrt(n) along a row for n in {0, 16, 32, 64, 128} chosen at run time (the same
+// for every lane of the wave; every lane must take part): a lane holds 32 consecutive values of
+// the row, and for n >= 64 the groups of 32 that make up a chunk sit in consecutive lanes (group g
+// of a 128-chunk in lane 4 k + g). Stages h = 1, 2, ..., n / 2 in that order -- h < 32 in
+// registers, h = 32 and 64 with lanes l ^ 1 and l ^ 2 -- then one multiply by RN(1/sqrt(n)).
+__device__ __forceinline__ void fwht_groups(float (&v)[32], int n) {
+    if (n == 0) return;
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1) {
+        if (h < n) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                if (!(i & h)) {
+                    const float a = v[i], b = v[i + h];
+                    v[i] = a + b;
+                    v[i + h] = a - b;
+                }
+            }
+        }
+    }
+    const int lane = __lane_id();
+    if (n >= 64) {
+        // lower lane: partner + self = a + b; upper lane: partner - self = a - b (one rounding)
+        const float sgn = (lane & 1) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf(v[i], sgn, lane_xor<1>(v[i]));
+    }
+    if (n >= 128) {
+        const float sgn = (lane & 2) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf(v[i], sgn, lane_xor<2>(v[i]));
+    }
+    const float c = n == 16 ? inv_sqrt_n<16>() : n == 32 ? inv_sqrt_n<32>() : n == 64 ? inv_sqrt_n<64>() : inv_sqrt_n<128>();
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = v[i] * c;
+}
+
 // Encode elements [OFF, OFF + B) of v into out (nibbles for E2M1: element j -> nibble j of the
 // 16-byte segment; bytes for E4M3). Scale arguments:
 //  pow2: the block scale is 2^k (k >= -126 after the caller's adjustment): the hardware convert

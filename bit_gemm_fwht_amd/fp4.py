@@ -250,8 +250,9 @@ def gemm(a: QTensor, b: QTensor, out_dtype=torch.bfloat16, out: torch.Tensor | N
          q_out: QTensor | None = None, keep_c: bool = True):
     """C [M, N] = A [M, K] * B [N, K]^T on quantized operands (fp32 accumulation).
 
-    With out_q (MX groups of 32 along N, E8M0 floor / ceil, RNE or SR), C is also quantized in the
-    epilogue and (C, C_q) is returned; keep_c=False skips writing C and returns (None, C_q)."""
+    With out_q (MX groups of 32 along N, E8M0 floor / ceil, RNE or SR, optionally rotated along N
+    with out_q.hadamard_n <= 128), C is also quantized in the epilogue and (C, C_q) is returned;
+    keep_c=False skips writing C and returns (None, C_q)."""
     dev = a.codes.device
     c = None
     if out_q is None or keep_c:

@@ -172,8 +172,11 @@ int fp4_hadamard(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int
  * list of the Quartet notes): if out_q is non-NULL, C_q->codes / C_q->scales (device, codes
  * 16-byte aligned) receive the fp32 result -- the value an fp32 C would hold -- quantized along N
  * exactly as fp4_quantize would quantize that fp32 C with *out_q: E2M1 or E4M3 elements, E8M0
- * floor or ceil scales, (1, 32) groups, RNE or SR (element (m, n) keyed by m * N + n), no
- * rotation. Requires N % 32 == 0; C_q->rows, cols, p are set to M, N, *out_q and tensor_scale to
+ * floor or ceil scales, (1, 32) groups, RNE or SR (element (m, n) keyed by m * N + n), and, with
+ * out_q->hadamard_n = n in {16, 32, 64, 128}, each n-chunk of a row of C rotated by H_n / sqrt(n)
+ * before it is quantized (an output that feeds the next layer's rotated GEMM; C itself is stored
+ * unrotated). Requires N % 32 == 0 and N % n == 0 (n = 256: FP4_ERR_UNSUPPORTED);
+ * C_q->rows, cols, p are set to M, N, *out_q and tensor_scale to
  * NULL. C may then be NULL (only the quantized output is written); out_q and C_q are given
  * together or not at all. workspace: fp4_gemm_workspace_bytes() bytes. */
 int64_t fp4_gemm_workspace_bytes(const fp4_qtensor* A, const fp4_qtensor* B);

@@ -136,7 +136,10 @@ def test_gemm_validation_without_device(fp4):
     assert run(None, cq) == E.ERR_INVALID_ARG                         # C_q without out_q
     assert run(P(fp4, block_cols=16), cq) == E.ERR_UNSUPPORTED         # only MX groups of 32
     assert run(P(fp4, block_cols=16, scale_mode=2), cq) == E.ERR_UNSUPPORTED
-    assert run(P(fp4, hadamard_n=128), cq) == E.ERR_UNSUPPORTED        # no rotation of C
+    assert run(P(fp4, hadamard_n=256), cq) == E.ERR_UNSUPPORTED        # rotation of C: n <= 128
+    assert run(P(fp4, hadamard_n=48), cq) == E.ERR_INVALID_ARG
+    b160 = qt(160, 256)
+    assert run(P(fp4, hadamard_n=64), cq, bb=b160) == E.ERR_INVALID_ARG  # N % n != 0
     assert run(P(fp4, round_mode=5), cq) == E.ERR_INVALID_ARG
     b100 = qt(100, 256)
     assert run(P(fp4), cq, bb=b100) == E.ERR_INVALID_ARG               # N % 32 != 0

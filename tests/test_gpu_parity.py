@@ -353,6 +353,48 @@ def test_gemm_fused_output_quantize(orc, M, N, K, kind):
             assert torch.equal(cq2.codes, cq.codes) and torch.equal(cq2.scales, cq.scales)
 
 
+@pytest.mark.parametrize("M,N,K,kind,hns", [
+    (200, 160, 384, "mxfp4", (16, 32)),     # small kernel, ragged M
+    (64, 128, 128, "mxfp8", (64, 128)),     # small kernel: a 128-chunk spans both wave columns
+    (512, 768, 1024, "mxfp4", (64, 128)),   # 256 x 256 kernel
+    (300, 640, 512, "nvfp4", (32, 128)),    # 256 x 256 kernel, ragged M, last tile half empty
+])
+def test_gemm_fused_output_quantize_rotated(orc, M, N, K, kind, hns):
+    """Epilogue rotation along N before the output quantize: the codes and scales equal the
+    oracle's quantization, with the same n, of the very fp32 C the call stores (rotation stages in
+    the oracle's order, so bit-exact); C itself is stored unrotated."""
+    rng = np.random.default_rng(M + 3 * N + K)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    if kind == "mxfp4":
+        pa, pb = P(), P(scale_mode=CEIL)
+    elif kind == "mxfp8":
+        pa, pb = P(elem=E4M3), P(elem=E4M3)
+    else:
+        pa, pb = P(block=(1, 16), scale_mode=NV46), P(block=(1, 16), scale_mode=NV)
+    ca, sa, ta = _orc_quant(orc, A, pa)
+    cb, sb, tb = _orc_quant(orc, B, pb)
+    qa = fp4.upload_qtensor(ca, sa, ta, M, K, pa, DEV)
+    qb = fp4.upload_qtensor(cb, sb, tb, N, K, pb, DEV)
+    c_plain = fp4.gemm(qa, qb, out_dtype=torch.float32)
+    for hn in hns:
+        for elem, sm, rnd in ((E2M1, FLOOR, RNE), (E2M1, CEIL, SR), (E4M3, CEIL, RNE)):
+            oq = P(elem=elem, scale_mode=sm, round_mode=rnd, seed=5, hadamard_n=hn)
+            c, cq = fp4.gemm(qa, qb, out_dtype=torch.float32, out_q=oq)
+            torch.cuda.synchronize()
+            assert torch.equal(c_plain.view(torch.int32), c.view(torch.int32))
+            oc, os_, _ = _orc_quant(orc, c.cpu().numpy(), oq)
+            gc, gs = cq.codes.cpu().numpy(), cq.scales.cpu().numpy()
+            oc, os_ = oc.reshape(-1), os_.reshape(-1).view(np.uint8)
+            bad = np.nonzero(gc != oc)[0]
+            assert bad.size == 0, f"{(hn, elem, sm, rnd)}: {bad.size} code bytes differ, first at {bad[:8]}"
+            bad = np.nonzero(gs != os_)[0]
+            assert bad.size == 0, f"{(hn, elem, sm, rnd)}: {bad.size} scale bytes differ, first at {bad[:8]}"
+            _, cq2 = fp4.gemm(qa, qb, out_q=oq, keep_c=False)
+            torch.cuda.synchronize()
+            assert torch.equal(cq2.codes, cq.codes) and torch.equal(cq2.scales, cq.scales)
+
+
 CW_CASES = [
     # dtype, rows, cols, params
     ("bf16", 256, 64, dict()),
