@@ -44,6 +44,32 @@ struct Cfg {
     static constexpr int LOADS = BM * CH / NT;     // 16-byte loads per thread per operand
 };
 
+// One K step's global loads of the 128 x 128 kernel: LOADS 16-byte pieces of A and of B per
+// thread (rows beyond M / N read as zero) and one scale dword (threads < 128: A's rows, else B's).
+template <bool FP8, bool B2D>
+__device__ __forceinline__ void small_gload(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb,
+                                            int64_t M, int64_t N, int64_t m0, int64_t n0, int64_t rowbytes,
+                                            int64_t kgroups, int kt, int tid, u32x4 (&ra)[Cfg<FP8>::LOADS],
+                                            u32x4 (&rb)[Cfg<FP8>::LOADS], uint32_t& rsa, uint32_t& rsb) {
+    using C = Cfg<FP8>;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+        const int ch = tid + NT * i, r = ch / C::CH, c = ch % C::CH;
+        const int64_t m = m0 + r, n = n0 + r;
+        const int64_t off = (int64_t)kt * C::RB + 16 * c;
+        ra[i] = m < M ? *reinterpret_cast<const u32x4*>(a + m * rowbytes + off) : (u32x4){0u, 0u, 0u, 0u};
+        rb[i] = n < N ? *reinterpret_cast<const u32x4*>(b + n * rowbytes + off) : (u32x4){0u, 0u, 0u, 0u};
+    }
+    if (tid < BM) {
+        const int64_t m = m0 + tid;
+        rsa = m < M ? *reinterpret_cast<const uint32_t*>(sa + m * kgroups + 4 * kt) : 0u;
+    } else {
+        const int64_t n = n0 + (tid - BM);
+        const int64_t srow = B2D ? (n >> 5) : n;
+        rsb = n < N ? *reinterpret_cast<const uint32_t*>(sb + srow * kgroups + 4 * kt) : 0u;
+    }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Fused output quantization ("online quantization" of the GEMM output in the QuTLASS kernel list
 // of the Quartet lecture notes), in both kernels' epilogues: C, as the fp32 values the plain output
@@ -70,41 +96,8 @@ __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
     const int64_t kgroups = g.K / 32;
     const int KT = (int)(g.K / BK);
 
-    uint4 ra[C::LOADS], rb[C::LOADS];
+    u32x4 ra[C::LOADS], rb[C::LOADS];
     uint32_t rsa = 0, rsb = 0;
-
-    auto gload = [&](int kt) {
-#pragma unroll
-        for (int i = 0; i < C::LOADS; ++i) {
-            const int ch = tid + NT * i, r = ch / C::CH, c = ch % C::CH;
-            const int64_t m = m0 + r, n = n0 + r;
-            const int64_t off = (int64_t)kt * C::RB + 16 * c;
-            ra[i] = m < g.M ? *reinterpret_cast<const uint4*>(g.a + m * rowbytes + off) : make_uint4(0, 0, 0, 0);
-            rb[i] = n < g.N ? *reinterpret_cast<const uint4*>(g.b + n * rowbytes + off) : make_uint4(0, 0, 0, 0);
-        }
-        if (tid < BM) {
-            const int64_t m = m0 + tid;
-            rsa = m < g.M ? *reinterpret_cast<const uint32_t*>(g.sa + m * kgroups + 4 * kt) : 0u;
-        } else {
-            const int64_t n = n0 + (tid - BM);
-            if (n < g.N) {
-                const int64_t srow = B2D ? (n >> 5) : n;
-                rsb = *reinterpret_cast<const uint32_t*>(g.sb + srow * kgroups + 4 * kt);
-            } else {
-                rsb = 0u;
-            }
-        }
-    };
-    auto lstore = [&]() {
-#pragma unroll
-        for (int i = 0; i < C::LOADS; ++i) {
-            const int ch = tid + NT * i, r = ch / C::CH, c = ch % C::CH;
-            *reinterpret_cast<uint4*>(sA + r * C::LD + 16 * c) = ra[i];
-            *reinterpret_cast<uint4*>(sB + r * C::LD + 16 * c) = rb[i];
-        }
-        if (tid < BM) sSA[tid] = rsa;
-        else sSB[tid - BM] = rsb;
-    };
 
     v4f acc[4][4];
 #pragma unroll
@@ -113,12 +106,21 @@ __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
         for (int j = 0; j < 4; ++j) acc[i][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
     const int fr = lane & 15, fg = lane >> 4;
-    gload(0);
+    const uint8_t *const ga = g.a, *const gb = g.b, *const gsa = g.sa, *const gsb = g.sb;
+    const int64_t M = g.M, N = g.N;
+    small_gload<FP8, B2D>(ga, gb, gsa, gsb, M, N, m0, n0, rowbytes, kgroups, 0, tid, ra, rb, rsa, rsb);
     for (int kt = 0; kt < KT; ++kt) {
         __syncthreads();
-        lstore();
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i) {
+            const int ch = tid + NT * i, r = ch / C::CH, c = ch % C::CH;
+            *reinterpret_cast<u32x4*>(sA + r * C::LD + 16 * c) = ra[i];
+            *reinterpret_cast<u32x4*>(sB + r * C::LD + 16 * c) = rb[i];
+        }
+        if (tid < BM) sSA[tid] = rsa;
+        else sSB[tid - BM] = rsb;
         __syncthreads();
-        if (kt + 1 < KT) gload(kt + 1);
+        if (kt + 1 < KT) small_gload<FP8, B2D>(ga, gb, gsa, gsb, M, N, m0, n0, rowbytes, kgroups, kt + 1, tid, ra, rb, rsa, rsb);
 
         v8i fa[4], fb[4];
         int sa_[4], sb_[4];
@@ -127,19 +129,19 @@ __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
             const int ra_ = wm * 64 + 16 * i + fr;  // A tile row (output m)
             const int rb_ = wn * 64 + 16 * i + fr;  // B tile row (output n)
             if constexpr (!FP8) {
-                const uint4 xa = *reinterpret_cast<const uint4*>(sA + ra_ * C::LD + 16 * fg);
-                const uint4 xb = *reinterpret_cast<const uint4*>(sB + rb_ * C::LD + 16 * fg);
-                fa[i] = (v8i){(int)xa.x, (int)xa.y, (int)xa.z, (int)xa.w, 0, 0, 0, 0};
-                fb[i] = (v8i){(int)xb.x, (int)xb.y, (int)xb.z, (int)xb.w, 0, 0, 0, 0};
+                const u32x4 xa = *reinterpret_cast<const u32x4*>(sA + ra_ * C::LD + 16 * fg);
+                const u32x4 xb = *reinterpret_cast<const u32x4*>(sB + rb_ * C::LD + 16 * fg);
+                fa[i] = (v8i){(int)xa[0], (int)xa[1], (int)xa[2], (int)xa[3], 0, 0, 0, 0};
+                fb[i] = (v8i){(int)xb[0], (int)xb[1], (int)xb[2], (int)xb[3], 0, 0, 0, 0};
             } else {
-                const uint4 xa0 = *reinterpret_cast<const uint4*>(sA + ra_ * C::LD + 16 * fg);
-                const uint4 xa1 = *reinterpret_cast<const uint4*>(sA + ra_ * C::LD + 64 + 16 * fg);
-                const uint4 xb0 = *reinterpret_cast<const uint4*>(sB + rb_ * C::LD + 16 * fg);
-                const uint4 xb1 = *reinterpret_cast<const uint4*>(sB + rb_ * C::LD + 64 + 16 * fg);
-                fa[i] = (v8i){(int)xa0.x, (int)xa0.y, (int)xa0.z, (int)xa0.w,
-                              (int)xa1.x, (int)xa1.y, (int)xa1.z, (int)xa1.w};
-                fb[i] = (v8i){(int)xb0.x, (int)xb0.y, (int)xb0.z, (int)xb0.w,
-                              (int)xb1.x, (int)xb1.y, (int)xb1.z, (int)xb1.w};
+                const u32x4 xa0 = *reinterpret_cast<const u32x4*>(sA + ra_ * C::LD + 16 * fg);
+                const u32x4 xa1 = *reinterpret_cast<const u32x4*>(sA + ra_ * C::LD + 64 + 16 * fg);
+                const u32x4 xb0 = *reinterpret_cast<const u32x4*>(sB + rb_ * C::LD + 16 * fg);
+                const u32x4 xb1 = *reinterpret_cast<const u32x4*>(sB + rb_ * C::LD + 64 + 16 * fg);
+                fa[i] = (v8i){(int)xa0[0], (int)xa0[1], (int)xa0[2], (int)xa0[3],
+                              (int)xa1[0], (int)xa1[1], (int)xa1[2], (int)xa1[3]};
+                fb[i] = (v8i){(int)xb0[0], (int)xb0[1], (int)xb0[2], (int)xb0[3],
+                              (int)xb1[0], (int)xb1[1], (int)xb1[2], (int)xb1[3]};
             }
             sa_[i] = (int)((sSA[ra_] >> (8 * fg)) & 0xFFu);
             sb_[i] = (int)((sSB[rb_] >> (8 * fg)) & 0xFFu);
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
             if constexpr (OUT == DT_F32) {
                 float* cp = reinterpret_cast<float*>(g.c) + m * g.ldc + n;
                 if (n + 3 < g.N && ((g.ldc & 3) == 0)) {
-                    *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
+                    *reinterpret_cast<f32x4*>(cp) = (f32x4){v[0], v[1], v[2], v[3]};
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
                 const uint32_t w0 = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
                 const uint32_t w1 = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
                 if (n + 3 < g.N && ((g.ldc & 3) == 0)) {
-                    *reinterpret_cast<uint2*>(cp) = make_uint2(w0, w1);
+                    *reinterpret_cast<u32x2*>(cp) = (u32x2){w0, w1};
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -695,14 +697,14 @@ __global__ __launch_bounds__(256) void k_nv_to_fp8(const uint8_t* codes, const u
     const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t groups = rows * (K / 32);
     if (gi >= groups) return;
-    const uint4 q = *reinterpret_cast<const uint4*>(codes + gi * 16);
+    const u32x4 q = *reinterpret_cast<const u32x4*>(codes + gi * 16);
     const uint32_t s01 = *reinterpret_cast<const uint16_t*>(scales + gi * 2);
     const float s0 = e4m3_value(s01 & 0x7Fu), s1 = e4m3_value((s01 >> 8) & 0x7Fu);
     const float S = fmaxf(s0, s1);
     // E = smallest exponent with 448 * 2^E >= 6 S (6 S is exact in fp32)
     const int E = e8m0_exp<8, 0x600000u>(6.0f * S, true);
     out_scales[gi] = (uint8_t)(E + 127);
-    const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+    const uint32_t qw[4] = {q[0], q[1], q[2], q[3]};
     uint32_t o[8];
     const float sc = E > -127 ? pow2f(E) : 1.0f;  // S = 0: every product is 0
 #pragma unroll
@@ -718,9 +720,9 @@ __global__ __launch_bounds__(256) void k_nv_to_fp8(const uint8_t* codes, const u
         o[2 * w] = r0;
         o[2 * w + 1] = r1;
     }
-    uint4* dst = reinterpret_cast<uint4*>(out + gi * 32);
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    u32x4* dst = reinterpret_cast<u32x4*>(out + gi * 32);
+    dst[0] = (u32x4){o[0], o[1], o[2], o[3]};
+    dst[1] = (u32x4){o[4], o[5], o[6], o[7]};
 }
 
 template <bool FP8, bool B2D, bool NVG, bool FQ>
