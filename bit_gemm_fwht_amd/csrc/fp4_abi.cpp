@@ -177,6 +177,57 @@ int fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int
     }
 }
 
+int fp4_quantize_batch(int32_t count, const fp4_quant_item* items, int32_t x_dtype, const fp4_qparams* p,
+                       void* stream) {
+    try {
+        if (count < 1 || count > kMaxBatch || !items || !p) return FP4_ERR_INVALID_ARG;
+        if (x_dtype != FP4_DT_F32 && x_dtype != FP4_DT_BF16) return FP4_ERR_INVALID_ARG;
+        const int sc = scale_class(p->scale_mode);
+        if (sc == SC_NV && !is_given(p->scale_mode)) return FP4_ERR_UNSUPPORTED;
+        const int esz = x_dtype == FP4_DT_BF16 ? 2 : 4;
+        SegArgs a[kMaxBatch] = {};
+        for (int i = 0; i < count; ++i) {
+            const fp4_quant_item& t = items[i];
+            Layout lay;
+            int rc = check_params(t.rows, t.cols, p, &lay);
+            if (rc != FP4_OK) return rc;
+            if (lay != L_SEG1D && lay != L_SEG2D) return FP4_ERR_UNSUPPORTED;
+            if (!t.x || !t.codes || !t.scales) return FP4_ERR_INVALID_ARG;
+            if (t.ldx < t.cols) return FP4_ERR_INVALID_ARG;
+            if (sc == SC_NV && !t.tensor_scale) return FP4_ERR_INVALID_ARG;
+            if (!aligned(t.x, 16) || (t.ldx * esz) % 16 || !aligned(t.codes, 16) || !aligned(t.scales, 8))
+                return FP4_ERR_ALIGNMENT;
+            a[i].x = t.x;
+            a[i].rows = t.rows;
+            a[i].cols = t.cols;
+            a[i].ldx = t.ldx;
+            a[i].nseg = t.rows * (t.cols / 32);
+            a[i].codes = reinterpret_cast<uint8_t*>(t.codes);
+            a[i].scales = t.scales;
+            a[i].tensor_scale = t.tensor_scale;
+            a[i].seed = p->seed;
+            a[i].ceil_rule = p->scale_mode == FP4_SCALE_E8M0_CEIL;
+            a[i].four_six = is_4over6(p->scale_mode);
+            a[i].nv_given = is_given(p->scale_mode);
+        }
+        // outputs must not alias each other or any input
+        for (int i = 0; i < count; ++i) {
+            const void* outs[2] = {items[i].codes, items[i].scales};
+            for (const void* o : outs) {
+                for (int j = 0; j < count; ++j) {
+                    if (o == items[j].x) return FP4_ERR_INVALID_ARG;
+                    if (j != i && (o == items[j].codes || o == items[j].scales)) return FP4_ERR_INVALID_ARG;
+                }
+            }
+            if (items[i].codes == items[i].scales) return FP4_ERR_INVALID_ARG;
+        }
+        return hip_status(launch_segment_batch(a, count, x_dtype, p->hadamard_n, p->elem, sc, p->round_mode,
+                                               p->block_rows, p->block_cols, reinterpret_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return FP4_ERR_INTERNAL;
+    }
+}
+
 int fp4_quantize_colwise(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                          const fp4_qparams* p, void* codes, void* scales, float* tensor_scale,
                          void* workspace, int64_t ws_bytes, void* stream) {

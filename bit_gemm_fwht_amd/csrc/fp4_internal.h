@@ -29,6 +29,15 @@ struct SegArgs {
     int colwise;
 };
 
+// Several tensors quantized with one mode in one launch: the workgroups of item i are
+// [start[i], start[i + 1]) (start[n] = the grid size); one item for every other launch.
+constexpr int kMaxBatch = 4;
+struct SegBatch {
+    SegArgs t[kMaxBatch];
+    uint32_t start[kMaxBatch];
+    int n;
+};
+
 struct RowArgs {
     const void* x;
     int64_t rows, cols, ldx;
@@ -52,6 +61,9 @@ struct DeqArgs {
 
 hipError_t launch_segment(const SegArgs& a, int in_dtype, int hn, int elem, int sc, int rnd, int br,
                           int bc, int pass, hipStream_t s);
+// PASS_QUANT of n <= kMaxBatch tensors sharing every mode parameter, in one launch
+hipError_t launch_segment_batch(const SegArgs* items, int n, int in_dtype, int hn, int elem, int sc, int rnd,
+                                int br, int bc, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
 hipError_t launch_amax_rows(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ldx,
                             uint32_t* ws, hipStream_t s);

@@ -265,8 +265,15 @@ __device__ __forceinline__ float f32_block(float (&v)[32], float amax, const uin
 // The segment kernel (1D groups, 2D tiles, amax pass, rotation pass)
 // ---------------------------------------------------------------------------------------------
 template <int IN, int HN, int ELEM, int SC, int RND, int BR, int BC, int PASS, bool TRX>
-__global__ __launch_bounds__(kThreads) void k_segment(SegArgs a) {
+__global__ __launch_bounds__(kThreads) void k_segment(SegBatch b) {
     constexpr int P = SegIO<IN>::P, ESZ = SegIO<IN>::ESZ;
+    // this workgroup's item of the batch and its workgroup index within the item (uniform)
+    int it = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxBatch; ++i)
+        if (i < b.n && blockIdx.x >= b.start[i]) it = i;
+    const SegArgs a = it == 0 ? b.t[0] : it == 1 ? b.t[1] : it == 2 ? b.t[2] : b.t[3];
+    const uint32_t blk = blockIdx.x - (it == 0 ? b.start[0] : it == 1 ? b.start[1] : it == 2 ? b.start[2] : b.start[3]);
     // column-wise view: workgroup tiles of TCW T-rows x SEGW segments (see load_block_segments_t)
     constexpr int SEGW = HN >= 256 ? 8 : 4, TCW = 4 * 64 / SEGW;
     static_assert(!TRX || (BR == 1 && PASS != PASS_ROTATE), "column-wise view: 1D groups only");
@@ -315,21 +322,21 @@ __global__ __launch_bounds__(kThreads) void k_segment(SegArgs a) {
     float v[32];
     if constexpr (TRX) {
         const int64_t ntt = (a.rows + TCW - 1) / TCW;
-        const int64_t tt = blockIdx.x % ntt, ts = blockIdx.x / ntt;
+        const int64_t tt = blk % ntt, ts = blk / ntt;
         const int64_t tr = tt * TCW + wv * (64 / SEGW) + lane / SEGW;
         sc = ts * SEGW + lane % SEGW;
         valid = tr < a.rows && sc < spr;
         seg = tr * spr + sc;
         load_block_segments_t<IN, SEGW>(a, tt, ts, reinterpret_cast<uint8_t*>(&stage[0][0]), v);
     } else if constexpr (BR == 1) {
-        const int64_t wbase = (int64_t)blockIdx.x * kThreads + 64 * wv;
+        const int64_t wbase = (int64_t)blk * kThreads + 64 * wv;
         seg = wbase + lane;
         valid = seg < a.nseg;
         load_wave_segments_1d<IN>(a, wbase, stage[wv], v);
     } else {
         // 2D: a workgroup covers 32 rows x 8 segments, wave wv rows 8 wv .. 8 wv + 7
         const int64_t ngc = (spr + 7) >> 3;
-        const int64_t R = blockIdx.x / (uint32_t)ngc, C = blockIdx.x - R * ngc;
+        const int64_t R = blk / (uint32_t)ngc, C = blk - R * ngc;
         row = R * 32 + 8 * wv + (lane >> 3);
         sc = C * 8 + (lane & 7);
         valid = sc < spr;
@@ -390,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void k_segment(SegArgs a) {
             } else {
                 const float amax_t = __uint_as_float(*a.ws);
                 g = amax_t > 0.0f ? amax_t / 2688.0f : 1.0f;
-                if (blockIdx.x == 0 && threadIdx.x == 0) *a.tensor_scale = g;
+                if (blk == 0 && threadIdx.x == 0) *a.tensor_scale = g;
             }
             const float m0 = block_amax<16, 0>(v), m1 = block_amax<16, 16>(v);
             const uint32_t s0 = nv_block<RND, 0>(v, m0, g, a.four_six != 0, rw, out);
@@ -654,29 +661,46 @@ __global__ __launch_bounds__(kThreads) void k_dequant_rowblock(DeqArgs a) {
         return hipGetLastError();                                                          \
     } while (0)
 
-template <int IN, int HN, int ELEM, int SC, int RND, int BR, int BC>
-static hipError_t launch_seg_q(const SegArgs& a, int pass, hipStream_t stream) {
+// workgroups of one item of a launch (the amax pass walks the tensor with at most 1024 of them)
+template <int HN, int BR>
+static int64_t seg_grid(const SegArgs& a, int pass) {
+    int64_t grid;
     if (a.colwise) {
+        constexpr int SEGW = HN >= 256 ? 8 : 4, TCW = 4 * 64 / SEGW;
+        grid = ((a.rows + TCW - 1) / TCW) * (((a.cols >> 5) + SEGW - 1) / SEGW);
+    } else if (BR == 1 || pass != PASS_QUANT) {
+        grid = (a.nseg + kThreads - 1) / kThreads;
+    } else {
+        grid = (a.rows / 32) * (((a.cols >> 5) + 7) >> 3);
+    }
+    if (pass == PASS_AMAX && grid > 1024) grid = 1024;
+    return grid;
+}
+
+template <int IN, int HN, int ELEM, int SC, int RND, int BR, int BC>
+static hipError_t launch_seg_q(SegBatch b, int pass, hipStream_t stream) {
+    // amax and rotation passes, and column-wise views, take one item
+    if ((pass != PASS_QUANT || b.t[0].colwise) && b.n != 1) return hipErrorInvalidValue;
+    int64_t grid = 0;
+    for (int i = 0; i < b.n; ++i) {
+        b.start[i] = (uint32_t)grid;
+        grid += seg_grid<HN, BR>(b.t[i], pass);
+    }
+    if (grid <= 0 || grid >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    if (b.t[0].colwise) {
         if constexpr (BR == 1) {
-            constexpr int SEGW = HN >= 256 ? 8 : 4, TCW = 4 * 64 / SEGW;
-            const int64_t grid = ((a.rows + TCW - 1) / TCW) * (((a.cols >> 5) + SEGW - 1) / SEGW);
-            if (pass == PASS_AMAX)
-                BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, 32, PASS_AMAX, true>), (grid < 1024 ? grid : 1024), a);
-            BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, BC, PASS_QUANT, true>), grid, a);
+            if (pass == PASS_AMAX) BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, 32, PASS_AMAX, true>), grid, b);
+            BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, BC, PASS_QUANT, true>), grid, b);
         }
         return hipErrorInvalidValue;
     }
-    int64_t grid;
-    if (BR == 1) grid = (a.nseg + kThreads - 1) / kThreads;
-    else grid = (a.rows / 32) * (((a.cols >> 5) + 7) >> 3);
-    // the amax pass walks the tensor with at most 1024 workgroups (one atomic each)
-    if (pass == PASS_AMAX) BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, 32, PASS_AMAX, false>), (grid < 1024 ? grid : 1024), a);
-    if (pass == PASS_ROTATE) BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, 32, PASS_ROTATE, false>), grid, a);
-    BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, BR, BC, PASS_QUANT, false>), grid, a);
+    if (pass == PASS_AMAX) BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, 32, PASS_AMAX, false>), grid, b);
+    if (pass == PASS_ROTATE) BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, 1, 32, PASS_ROTATE, false>), grid, b);
+    BGF_LAUNCH((k_segment<IN, HN, ELEM, SC, RND, BR, BC, PASS_QUANT, false>), grid, b);
 }
 
 template <int IN, int HN>
-static hipError_t dispatch_seg_hn(const SegArgs& a, int elem, int sc, int rnd, int br, int bc,
+static hipError_t dispatch_seg_hn(const SegBatch& a, int elem, int sc, int rnd, int br, int bc,
                                   int pass, hipStream_t s) {
     if (pass != PASS_QUANT) return launch_seg_q<IN, HN, ELEM_E2M1, SC_E8M0, RND_RNE, 1, 32>(a, pass, s);
 #define BGF_RB(E, S, R)                                                                    \
@@ -715,8 +739,8 @@ static hipError_t dispatch_seg_hn(const SegArgs& a, int elem, int sc, int rnd, i
 #undef BGF_RB
 }
 
-hipError_t launch_segment(const SegArgs& a, int in_dtype, int hn, int elem, int sc, int rnd, int br,
-                          int bc, int pass, hipStream_t s) {
+static hipError_t launch_batch(const SegBatch& a, int in_dtype, int hn, int elem, int sc, int rnd, int br,
+                               int bc, int pass, hipStream_t s) {
 #define BGF_HN(IN)                                                                         \
     switch (hn) {                                                                          \
         case 0: return dispatch_seg_hn<IN, 0>(a, elem, sc, rnd, br, bc, pass, s);          \
@@ -730,6 +754,23 @@ hipError_t launch_segment(const SegArgs& a, int in_dtype, int hn, int elem, int 
     if (in_dtype == DT_BF16) { BGF_HN(DT_BF16) }
     BGF_HN(DT_F32)
 #undef BGF_HN
+}
+
+hipError_t launch_segment(const SegArgs& a, int in_dtype, int hn, int elem, int sc, int rnd, int br,
+                          int bc, int pass, hipStream_t s) {
+    SegBatch b{};
+    b.t[0] = a;
+    b.n = 1;
+    return launch_batch(b, in_dtype, hn, elem, sc, rnd, br, bc, pass, s);
+}
+
+hipError_t launch_segment_batch(const SegArgs* items, int n, int in_dtype, int hn, int elem, int sc, int rnd,
+                                int br, int bc, hipStream_t s) {
+    if (n < 1 || n > kMaxBatch) return hipErrorInvalidValue;
+    SegBatch b{};
+    for (int i = 0; i < n; ++i) b.t[i] = items[i];
+    b.n = n;
+    return launch_batch(b, in_dtype, hn, elem, sc, rnd, br, bc, PASS_QUANT, s);
 }
 
 hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream) {

@@ -44,6 +44,12 @@ class QTensorC(ctypes.Structure):
                 ("cols", ctypes.c_int64), ("p", QParams)]
 
 
+class QuantItemC(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("ldx", ctypes.c_int64), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("tensor_scale", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -68,6 +74,9 @@ def lib() -> ctypes.CDLL:
     L.fp4_quantize.argtypes = [P, I32, I64, I64, I64, QP, P, P, P, P, I64, P]
     L.fp4_quantize.restype = ctypes.c_int
     L.fp4_quantize_colwise.argtypes = [P, I32, I64, I64, I64, QP, P, P, P, P, I64, P]
+    L.fp4_quantize_colwise.restype = ctypes.c_int
+    L.fp4_quantize_batch.argtypes = [I32, ctypes.POINTER(QuantItemC), I32, QP, P]
+    L.fp4_quantize_batch.restype = ctypes.c_int
     L.fp4_quantize_colwise.restype = ctypes.c_int
     L.fp4_dequantize.argtypes = [P, P, P, I64, I64, QP, P, I32, I64, P]
     L.fp4_dequantize.restype = ctypes.c_int
@@ -189,6 +198,34 @@ def quantize(x: torch.Tensor, params: Params = MXFP4, out: QTensor | None = None
                             _stream_ptr(x.device))
     _check(st, "fp4_quantize")
     return q
+
+
+def quantize_batch(xs, params: Params = MXFP4, outs=None, tensor_scales=None) -> list:
+    """Quantize up to four 2-D CUDA tensors of one dtype with the same params in one launch (the
+    same codes and scales as quantize() of each). tensor_scales: per-tensor g for the _GIVEN
+    NVFP4 modes."""
+    n = len(xs)
+    if n == 0:
+        return []
+    outs = list(outs) if outs is not None else [None] * n
+    tss = list(tensor_scales) if tensor_scales is not None else [None] * n
+    items = (QuantItemC * n)()
+    qs = []
+    for i, x in enumerate(xs):
+        if x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+            raise ValueError("each x must be a 2-D CUDA tensor, contiguous along its last axis")
+        if x.dtype != xs[0].dtype:
+            raise ValueError("all tensors of a batch share one dtype")
+        rows, cols = x.shape
+        q = outs[i] if outs[i] is not None else empty_qtensor(rows, cols, params, x.device)
+        _set_given_scale(q, params, tss[i])
+        ts = q.tensor_scale.data_ptr() if q.tensor_scale is not None else None
+        items[i] = QuantItemC(x.data_ptr(), rows, cols, x.stride(0), q.codes.data_ptr(), q.scales.data_ptr(), ts)
+        qs.append(q)
+    p = params.c()
+    st = lib().fp4_quantize_batch(n, items, _dtype_code(xs[0]), ctypes.byref(p), _stream_ptr(xs[0].device))
+    _check(st, "fp4_quantize_batch")
+    return qs
 
 
 def quantize_colwise(x: torch.Tensor, params: Params = MXFP4, out: QTensor | None = None,

@@ -135,6 +135,26 @@ int fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int
                  const fp4_qparams* p, void* codes, void* scales, float* tensor_scale,
                  void* workspace, int64_t ws_bytes, void* stream);
 
+/* One tensor of a batched quantize: x [rows, cols] with leading dimension ldx, its codes, scales
+ * and tensor_scale (an input, the tensor scale g, in the _GIVEN NVFP4 modes; else unused). */
+typedef struct {
+    const void* x;
+    int64_t rows, cols, ldx;
+    void* codes;
+    void* scales;
+    float* tensor_scale;
+} fp4_quant_item;
+
+/* Batched quantization: the same result as fp4_quantize(items[i].x, x_dtype, ..., p, ...) for each
+ * i, in one launch (one ramp and one tail instead of count, e.g. a layer's activations and weights
+ * quantized with one recipe). 1 <= count <= 4; every item shares x_dtype and *p (SR keys each item
+ * by its own element index, as separate calls with p->seed would). Modes that need a tensor-wide
+ * amax first (NVFP4 and 4/6 without a given tensor scale, per-tensor blocks) and per-row blocks
+ * return FP4_ERR_UNSUPPORTED; requirements and alignment per item as for fp4_quantize; no output
+ * may alias any item's input or another output. No workspace. */
+int fp4_quantize_batch(int32_t count, const fp4_quant_item* items, int32_t x_dtype, const fp4_qparams* p,
+                       void* stream);
+
 /* Column-wise quantization: quantize T = x^T without forming it. x is [rows, cols] (row pitch ldx);
  * the result is exactly fp4_quantize of the [cols, rows] tensor T with *p: codes, scales and the
  * rotation run along x's rows (T's contiguous axis), e.g. to feed dW = dY^T X, whose contraction

@@ -101,6 +101,40 @@ def test_quantize_validation_without_device(fp4):
     assert _quant(fp4, P(fp4), codes=0x1000) == E.ERR_INVALID_ARG      # aliasing
 
 
+def test_quantize_batch_validation_without_device(fp4):
+    """Batched quantize: every rejection happens on the host, before any HIP call."""
+    E = fp4
+    L = fp4.lib()
+
+    def items(*specs):
+        arr = (fp4.QuantItemC * max(len(specs), 1))()
+        for i, sp in enumerate(specs):
+            base = dict(x=0x10000 * (i + 1), rows=64, cols=256, ldx=256, codes=0x100000 * (i + 1),
+                        scales=0x1000000 * (i + 1), tensor_scale=None)
+            base.update(sp)
+            arr[i] = fp4.QuantItemC(**base)
+        return arr
+
+    def run(arr, n, p, dtype=1):
+        return L.fp4_quantize_batch(n, arr, dtype, ctypes.byref(p), None)
+
+    two = items({}, {"rows": 96})
+    assert run(two, 0, P(fp4)) == E.ERR_INVALID_ARG                       # empty batch
+    five = items({}, {}, {}, {}, {})
+    assert run(five, 5, P(fp4)) == E.ERR_INVALID_ARG                      # more than four
+    assert run(two, 2, P(fp4), dtype=7) == E.ERR_INVALID_ARG
+    assert run(two, 2, P(fp4, block_cols=16, scale_mode=2)) == E.ERR_UNSUPPORTED   # NV needs an amax pass
+    assert run(two, 2, P(fp4, block_cols=16, scale_mode=5)) == E.ERR_INVALID_ARG   # given g missing
+    assert run(two, 2, P(fp4, block_cols=256)) == E.ERR_UNSUPPORTED        # per-row blocks
+    assert run(items({}, {"cols": 250, "ldx": 250}), 2, P(fp4)) == E.ERR_INVALID_ARG
+    assert run(items({}, {"x": None}), 2, P(fp4)) == E.ERR_INVALID_ARG
+    assert run(items({}, {"ldx": 100}), 2, P(fp4)) == E.ERR_INVALID_ARG
+    assert run(items({}, {"codes": 0x100008}), 2, P(fp4)) == E.ERR_ALIGNMENT
+    assert run(items({}, {"codes": 0x10000}), 2, P(fp4)) == E.ERR_INVALID_ARG    # output = other input
+    assert run(items({}, {"scales": 0x100000}), 2, P(fp4)) == E.ERR_INVALID_ARG  # outputs alias
+    assert run(items({}, {"rows": 48}), 2, P(fp4, block_rows=32)) == E.ERR_INVALID_ARG  # 2D: rows % 32
+
+
 def test_gemm_validation_without_device(fp4):
     E = fp4
     L = fp4.lib()

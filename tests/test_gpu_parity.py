@@ -395,6 +395,43 @@ def test_gemm_fused_output_quantize_rotated(orc, M, N, K, kind, hns):
             assert torch.equal(cq2.codes, cq.codes) and torch.equal(cq2.scales, cq.scales)
 
 
+BATCH_CASES = [
+    # dtype, shapes, params
+    ("bf16", [(4096 // 16, 4096 // 8), (11008 // 43, 4096 // 8)], dict(hadamard_n=128)),
+    ("f32", [(96, 256), (40, 64), (200, 160)], dict(scale_mode=CEIL, round_mode=SR, seed=9, hadamard_n=32)),
+    ("bf16", [(64, 512), (128, 256)], dict(block=(32, 32), scale_mode=CEIL, hadamard_n=64)),
+    ("bf16", [(33, 128), (64, 96), (8, 32), (130, 256)], dict(elem=E4M3, round_mode=SR, seed=2)),
+    ("f32", [(64, 128), (96, 64)], dict(block=(1, 16), scale_mode=fp4.SCALE_NV_4OVER6_GIVEN)),
+    ("bf16", [(64, 256), (32, 64)], dict(block=(1, 16), scale_mode=F32, hadamard_n=16)),
+]
+
+
+@pytest.mark.parametrize("dt,shapes,kw", BATCH_CASES)
+def test_quantize_batch_parity(orc, dt, shapes, kw):
+    """One launch over several tensors gives, for each, the codes and scales of its own
+    fp4_quantize call, and those equal the oracle's."""
+    rng = np.random.default_rng(len(shapes) * 100 + shapes[0][0])
+    params = P(**kw)
+    given = params.scale_mode == fp4.SCALE_NV_4OVER6_GIVEN
+    xs, gs = [], []
+    for r, c in shapes:
+        x = (rng.standard_normal((r, c)) * rng.uniform(0.01, 100)).astype(np.float32)
+        gs.append(float(np.abs(x).max()) / 2688 * 0.8 if given else None)
+        xs.append(wl.f32_to_bf16_bits(x) if dt == "bf16" else x)
+    xt = [_to_dev(x) for x in xs]
+    qs = fp4.quantize_batch(xt, params, tensor_scales=gs if given else None)
+    torch.cuda.synchronize()
+    for i, (x, q) in enumerate(zip(xs, qs)):
+        one = fp4.quantize(xt[i], params, tensor_scale=gs[i])
+        torch.cuda.synchronize()
+        assert torch.equal(q.codes, one.codes) and torch.equal(q.scales, one.scales), f"item {i}"
+        oc, os_, _ = orc.quantize(x, elem=params.elem, block=params.block, scale_mode=params.scale_mode,
+                                  round_mode=params.round_mode, hadamard_n=params.hadamard_n, seed=params.seed,
+                                  tensor_scale=gs[i])
+        assert np.array_equal(q.codes.cpu().numpy(), oc.reshape(-1)), f"item {i} codes"
+        assert np.array_equal(q.scales.cpu().numpy(), os_.reshape(-1).view(np.uint8)), f"item {i} scales"
+
+
 CW_CASES = [
     # dtype, rows, cols, params
     ("bf16", 256, 64, dict()),
