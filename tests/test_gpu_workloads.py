@@ -51,11 +51,16 @@ def _sampled_gemm(orc, qa, qb, oa, ob, pa, pb, c_dtype, n=2048, seed=0):
 
 
 def test_llama7b_forward_linear(orc):
-    """X 4096x4096, W 11008x4096 (bf16), H_128 + MXFP4; 4096x11008x4096 GEMM to bf16."""
+    """X 4096x4096, W 11008x4096 (bf16), H_128 + MXFP4; 4096x11008x4096 GEMM to bf16. The operands
+    are quantized as the benchmark does it, X and W in one batched launch."""
     x, w, _ = wl.llama_linear(0)
     p = P(hadamard_n=128)
-    qx, ox = _quant_both(orc, x, p)
-    qw, ow = _quant_both(orc, w, p)
+    qx, qw = fp4.quantize_batch([_to_dev(x), _to_dev(w)], p)
+    torch.cuda.synchronize()
+    ox, ow = _orc_quant(orc, x, p), _orc_quant(orc, w, p)
+    for q, o in ((qx, ox), (qw, ow)):
+        assert np.array_equal(q.codes.cpu().numpy(), o[0].reshape(-1)), "codes differ from the oracle"
+        assert np.array_equal(q.scales.cpu().numpy(), o[1].reshape(-1).view(np.uint8)), "scales differ"
     _sampled_gemm(orc, qx, qw, ox, ow, p, p, torch.bfloat16)
 
 
