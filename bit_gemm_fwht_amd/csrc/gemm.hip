@@ -341,23 +341,29 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
     const int64_t kgroups = g.K / 32;
     const int KT = (int)(g.K / C::KSTEP);
 
-    // Direct-to-LDS copies go through buffer resources: base + 32-bit byte offset, with the K
-    // position and the row step in the scalar offset. Offsets past the end of an operand (rows
-    // beyond M or N) read as zero; those rows only feed outputs that are never stored.
+    // Direct-to-LDS copies go through buffer resources: base + 32-bit byte offset. The row part of
+    // every offset sits in the per-lane (vector) offset, which the range check covers, so rows
+    // beyond M or N read as zero (they only feed outputs that are never stored); the scalar offset
+    // only adds the K position within a row.
     const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, (int)(g.M * rowbytes), 0x00020000);
     const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)g.b, (short)0, (int)(g.N * rowbytes), 0x00020000);
     const __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc((void*)g.sa, (short)0, (int)(g.M * kgroups), 0x00020000);
     const __amdgpu_buffer_rsrc_t rSB = __builtin_amdgcn_make_buffer_rsrc(
         (void*)g.sb, (short)0, (int)((B2D ? (g.N + 31) / 32 : g.N) * kgroups), 0x00020000);
+    // extent 0: every read through it is out of range and returns zeros
+    const __amdgpu_buffer_rsrc_t rZ = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, 0, 0x00020000);
     // copy i of this wave fills LDS rows r = (wave * IPW + i) * 8 + lane / 8, slot lane % 8, with
-    // chunk slot ^ swz(r) = slot ^ (lane / 8) ^ (i & 1) of the row (IPW is even)
+    // chunk slot ^ swz(r) = slot ^ (lane / 8) ^ (i & 1) of the row (IPW is even); wave * IPW * 8 is
+    // a multiple of 16, so swz(r) = (lane / 8) ^ (i & 1)
     const int r0 = wave * C::IPW * 8 + (lane >> 3);
-    int voA[2], voB[2];
+    // (a literal bound: with the dependent C::IPW here the host pass silently drops the kernel stub)
+    static_assert(C::IPW == 4, "four 1 KB copies per wave and operand");
+    int voA[4], voB[4];
 #pragma unroll
-    for (int par = 0; par < 2; ++par) {
-        const int c = (lane & 7) ^ ((lane >> 3) & 7) ^ par;
-        voA[par] = (int)((m0 + r0) * rowbytes + 16 * c);
-        voB[par] = (int)((n0 + r0) * rowbytes + 16 * c);
+    for (int i = 0; i < C::IPW; ++i) {
+        const int c = (lane & 7) ^ ((lane >> 3) & 7) ^ (i & 1);
+        voA[i] = (int)((m0 + r0 + 8 * i) * rowbytes + 16 * c);
+        voB[i] = (int)((n0 + r0 + 8 * i) * rowbytes + 16 * c);
     }
     // scale dwords: the stage holds SPR bytes of each of A's and B's 256 rows, row-major, as
     // consecutive dwords; waves take them in order, A's first
@@ -380,28 +386,31 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
     // stage, so that no wave stalls on a full address FIFO with all its copies at once (part p:
     // A and B copies i in [p IPW / NKK, (p + 1) IPW / NKK); the scales with part 0).
     static_assert(C::IPW % C::NKK == 0, "copies per step");
-    // Stage KT (one past the last) is a dummy: its offsets lie past every buffer's extent, so the
-    // copies read nothing and write zeros into the free stage buffer.
+    // Stage KT (one past the last) is a dummy: its copies go through the zero-extent resource, so
+    // they read nothing and write zeros into the free stage buffer.
     auto issue_part = [&](int kt, int part) {
         uint8_t* st = smem + (kt % C::NST) * C::STAGE;
-        const int so = kt < KT ? kt * C::RB : (1 << 30), ss = kt < KT ? kt * C::SPR : (1 << 30);
+        const bool real = kt < KT;
+        const int so = real ? kt * C::RB : 0, ss = real ? kt * C::SPR : 0;
+        const __amdgpu_buffer_rsrc_t qA = real ? rA : rZ, qB = real ? rB : rZ;
+        const __amdgpu_buffer_rsrc_t qSA = real ? rSA : rZ, qSB = real ? rSB : rZ;
         constexpr int IPP = C::IPW / C::NKK;
 #pragma unroll
         for (int ii = 0; ii < IPP; ++ii) {
             const int i = part * IPP + ii;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(st + C::OFF_A + (wave * C::IPW + i) * 1024), 16,
-                                                     voA[i & 1], so + (int)(8 * i * rowbytes), 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(st + C::OFF_B + (wave * C::IPW + i) * 1024),
-                                                     16, voB[i & 1], so + (int)(8 * i * rowbytes), 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qA, (lds_ptr_t)(st + C::OFF_A + (wave * C::IPW + i) * 1024), 16,
+                                                     voA[i], so, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qB, (lds_ptr_t)(st + C::OFF_B + (wave * C::IPW + i) * 1024),
+                                                     16, voB[i], so, 0, 0);
         }
         if (part != 0) return;
 #pragma unroll
         for (int j = 0; j < C::SPW; ++j) {
             if ((wave * C::SPW + j) * 64 >= C::SB / 4)  // wave-uniform
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rSB, (lds_ptr_t)(st + (wave * C::SPW + j) * 256),
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(qSB, (lds_ptr_t)(st + (wave * C::SPW + j) * 256),
                                                          4, voS[j], ss, 0, 0);
             else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_ptr_t)(st + (wave * C::SPW + j) * 256),
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(qSA, (lds_ptr_t)(st + (wave * C::SPW + j) * 256),
                                                          4, voS[j], ss, 0, 0);
         }
     };
