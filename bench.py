@@ -1,20 +1,27 @@
-"""Benchmark of the quantize + MXFP4 GEMM hot path on one MI355X.
+"""Benchmark of the quantize + block-scaled GEMM hot path on one MI355X.
 
-One step = the whole path over one batch of a Llama-7B-shaped forward linear:
+Default workload (the headline): one step = the whole path over one batch of a Llama-7B-shaped
+forward linear:
   X bf16 [4096, 4096] (N(0,1), 1% of channels x20) and W bf16 [11008, 4096] (N(0, 0.02^2)),
   both rotated along K by blockwise H_128 / sqrt(128) and quantized to MXFP4 (E2M1 elements,
   one E8M0 floor scale per 32, round to nearest even) in one batched launch, then C = X W^T on the
   MXFP4 operands, fp32 accumulation, bf16 output.
-Inputs are resident in HBM before timing starts; the step cycles over several copies of X and W
+`--workload` selects one of the other full-size workloads instead (same JSON layout):
+  backward_2d        dX = dY W^T, 8192 x 4096 x 4096: W 2D 32x32 truncation-free RNE, dY group-32
+                     truncation-free with Philox stochastic rounding (seed 7), both H_128; MXFP4
+  backward_2d_mxfp8  the same with E4M3 elements (MXFP8, the FP8 matrix cores)
+  nvfp4_4over6       8192^3: X Laplace with 0.1% x30 outliers, W N(0, 0.02^2), NVFP4 with the
+                     4/6 choice (tensor amax pass + quantize), GEMM through the FP8 re-expression
+Inputs are resident in HBM before timing starts; the step cycles over several copies of the inputs
 (more than the 256 MB last-level cache) so that every step reads its inputs from HBM.
 
 Prints one JSON line. `value` is the step's effective throughput in TFLOP/s (GEMM FLOPs over the
 whole step time, quantization included); the per-kernel GB/s / TFLOP/s and roofline fractions are
 in the extra fields. `roofline` is the dominant kernel (the GEMM): algorithmic FLOPs per launch over
 its average launch time from HIP events on the launch stream; its `traffic` is the measured memory
-traffic per launch from the committed counter summary, reported only while the summary's kernel
-source hash matches the current source. `cpu_baseline` times the CPU oracle on a bounded sample of
-the same step.
+traffic per launch from the committed counter summary (headline workload only), reported only while
+the summary's kernel source hash matches the current source. `cpu_baseline` times the CPU oracle on
+a bounded sample of the same step.
 
 `--copy-calibration MIB` instead runs only a plain device-to-device copy of MIB MiB a few times
 (the reference kernel whose FETCH_SIZE / WRITE_SIZE counter readings calibrate the GEMM's).
@@ -33,11 +40,33 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 FP4_PEAK_TFLOPS = 10100.0       # MI355X dense MXFP4 matrix throughput, TFLOP/s
-M, N, K = 4096, 11008, 4096
-HN = 128
+FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8 matrix throughput, TFLOP/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 GEMM_SRC = os.path.join(ROOT, "bit_gemm_fwht_amd", "csrc", "gemm.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_llama7b_forward_linear_traffic.md")
+HEADLINE = "llama7b_forward_linear"
+
+# name -> shapes (C = A B^T: A [M, K], B [N, K]), quantization of A and B, CPU-sample fraction
+WORKLOADS = {
+    "llama7b_forward_linear": dict(
+        M=4096, N=11008, K=4096, a=dict(hadamard_n=128), b=dict(hadamard_n=128), batched=True,
+        quant="E2M1 + E8M0 per 32 (floor), RNE", fp8=False, f=0.25,
+        kernel="k_gemm_big (MXFP4, 256x256 tiles, 32x32x64 scaled MFMA, bf16 out)"),
+    "backward_2d": dict(
+        M=8192, N=4096, K=4096, a=dict(hadamard_n=128, scale="ceil", sr=True),
+        b=dict(hadamard_n=128, block=(32, 32), scale="ceil"), batched=False,
+        quant="dY: E2M1 + E8M0 per 32 (ceil), Philox SR; W: E2M1 + E8M0 per 32x32 (ceil), RNE",
+        fp8=False, f=0.25, kernel="k_gemm_big (MXFP4, 2D B scales, 256x256 tiles, bf16 out)"),
+    "backward_2d_mxfp8": dict(
+        M=8192, N=4096, K=4096, a=dict(hadamard_n=128, scale="ceil", sr=True, e4m3=True),
+        b=dict(hadamard_n=128, scale="ceil", e4m3=True), batched=False,
+        quant="dY: E4M3 + E8M0 per 32 (ceil), Philox SR; W: E4M3 + E8M0 per 32 (ceil), RNE",
+        fp8=True, f=0.25, kernel="k_gemm_big (MXFP8, 256x256 tiles, 32x32x64 scaled MFMA, bf16 out)"),
+    "nvfp4_4over6": dict(
+        M=8192, N=8192, K=8192, a=dict(nv46=True), b=dict(nv46=True), batched=False,
+        quant="E2M1 + E4M3 per 16 x fp32 tensor scale, 4/6 choice, RNE", fp8=True, f=0.125,
+        kernel="fp4_gemm call: two NVFP4->FP8 re-expression passes + k_gemm_big (FP8, bf16 out)"),
+}
 
 
 def parse():
@@ -45,13 +74,36 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--copies", type=int, default=4, help="input copies cycled through (> LLC)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-fraction", type=float, default=0.25,
-                    help="fraction f of X rows and W rows the CPU oracle processes")
+    ap.add_argument("--cpu-fraction", type=float, default=None,
+                    help="fraction f of A rows and B rows the CPU oracle processes")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
+
+
+def params_of(fp4, spec):
+    """fp4.Params for one operand's quantization spec."""
+    if spec.get("nv46"):
+        return fp4.Params(block=(1, 16), scale_mode=fp4.SCALE_NV_4OVER6)
+    return fp4.Params(elem=fp4.E4M3 if spec.get("e4m3") else fp4.E2M1, block=spec.get("block", (1, 32)),
+                      scale_mode=fp4.SCALE_E8M0_CEIL if spec.get("scale") == "ceil" else fp4.SCALE_E8M0_FLOOR,
+                      round_mode=fp4.ROUND_SR if spec.get("sr") else fp4.ROUND_RNE,
+                      hadamard_n=spec.get("hadamard_n", 0), seed=7 if spec.get("sr") else 0)
+
+
+def inputs_of(name):
+    """Host bf16 bit patterns (A, B) of a workload: A [M, K] is the left operand."""
+    from bit_gemm_fwht_amd import workloads as wl
+    if name == "llama7b_forward_linear":
+        x, w, _ = wl.llama_linear(0)
+        return x, w
+    if name.startswith("backward_2d"):
+        w, dy = wl.backward_2d(0)
+        return dy, w
+    return wl.nvfp4_4over6(0)
 
 
 def measured_traffic():
@@ -80,30 +132,41 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
-def cpu_baseline(x_bits, w_bits, f):
-    """Time the oracle on f*M rows of X, f*N rows of W and the f*M x f*N block of C, and scale to
+def cpu_baseline(wk, a_bits, b_bits, pa, pb, f):
+    """Time the oracle on f*M rows of A, f*N rows of B and the f*M x f*N block of C, and scale to
     a whole step: T = T_quantize / f + T_gemm / f^2."""
     import oracle as orc
-    sm, sn = max(int(M * f), 1), max(int(N * f), 1)
-    xs = np.ascontiguousarray(x_bits[:sm])
-    ws = np.ascontiguousarray(w_bits[:sn])
+    M, N, K = wk["M"], wk["N"], wk["K"]
+    sm, sn = max(int(M * f) // 32 * 32, 32), max(int(N * f) // 32 * 32, 32)  # whole 32-row tiles
+    As = np.ascontiguousarray(a_bits[:sm])
+    Bs = np.ascontiguousarray(b_bits[:sn])
+
+    def q(x, p):
+        return orc.quantize(x, elem=p.elem, block=p.block, scale_mode=p.scale_mode,
+                            round_mode=p.round_mode, hadamard_n=p.hadamard_n, seed=p.seed)
+
     t0 = time.perf_counter()
-    ca, sa, _ = orc.quantize(xs, hadamard_n=HN)
-    cb, sb, _ = orc.quantize(ws, hadamard_n=HN)
+    ca, sa, ta = q(As, pa)
+    cb, sb, tb = q(Bs, pb)
     t1 = time.perf_counter()
-    a64 = orc.operand_f64(ca, sa, None, sm, K)
-    b64 = orc.operand_f64(cb, sb, None, sn, K)
+    a64 = orc.operand_f64(ca, sa, ta, sm, K, elem=pa.elem, block=pa.block, scale_mode=pa.scale_mode)
+    if pb.block[0] == 1:
+        b64 = orc.operand_f64(cb, sb, tb, sn, K, elem=pb.elem, block=pb.block, scale_mode=pb.scale_mode)
+    else:  # 2D tiles: each row takes its tile row's scales
+        srow = np.ascontiguousarray(sb.reshape(sn // 32, -1)[np.arange(sn) // 32])
+        b64 = orc.operand_f64(cb, srow, tb, sn, K, elem=pb.elem, block=(1, 32), scale_mode=pb.scale_mode)
     orc.gemm_f64(a64, b64)
     t2 = time.perf_counter()
-    t_step = (t1 - t0) / f + (t2 - t1) / (f * f)
+    fm, fn = sm / M, sn / N
+    t_step = (t1 - t0) / ((fm + fn) / 2) + (t2 - t1) / (fm * fn)
     return {
         "value": round(2.0 * M * N * K / t_step / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"oracle quantize of {sm} X rows + {sn} W rows ({t1 - t0:.2f} s) and the fp64 "
+        "sample": (f"oracle quantize of {sm} A rows + {sn} B rows ({t1 - t0:.2f} s) and the fp64 "
                    f"GEMM of their {sm}x{sn} block over K={K} ({t2 - t1:.2f} s), scaled to a full "
-                   f"step as T_q/f + T_gemm/f^2 with f={f}"),
+                   f"step as T_q/f + T_gemm/f^2 with f={f} (the sampled row fractions)"),
         "step_s": round(t_step, 3),
     }
 
@@ -120,19 +183,31 @@ def main():
     import torch
 
     from bit_gemm_fwht_amd import fp4
-    from bit_gemm_fwht_amd import workloads as wl
 
     fp4.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
-    x_bits, w_bits, _ = wl.llama_linear(0, m=M, n=N, k=K)
-    x0 = torch.from_numpy(x_bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    w0 = torch.from_numpy(w_bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    xs = [x0] + [x0.clone() for _ in range(args.copies - 1)]
-    ws = [w0] + [w0.clone() for _ in range(args.copies - 1)]
-    params = fp4.Params(hadamard_n=HN)
-    qx = [fp4.empty_qtensor(M, K, params, dev) for _ in range(args.copies)]
-    qw = [fp4.empty_qtensor(N, K, params, dev) for _ in range(args.copies)]
+    wk = WORKLOADS[args.workload]
+    M, N, K = wk["M"], wk["N"], wk["K"]
+    pa, pb = params_of(fp4, wk["a"]), params_of(fp4, wk["b"])
+    a_bits, b_bits = inputs_of(args.workload)
+    a0 = torch.from_numpy(a_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    b0 = torch.from_numpy(b_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    As = [a0] + [a0.clone() for _ in range(args.copies - 1)]
+    Bs = [b0] + [b0.clone() for _ in range(args.copies - 1)]
+    qa = [fp4.empty_qtensor(M, K, pa, dev) for _ in range(args.copies)]
+    qb = [fp4.empty_qtensor(N, K, pb, dev) for _ in range(args.copies)]
     cs = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(args.copies)]
+    # workspaces allocated once, outside the timed region
+    wsa = wsb = wsg = None
+    nb = fp4.buffer_sizes(M, K, pa)[2]
+    if nb:
+        wsa = torch.empty(nb, dtype=torch.uint8, device=dev)
+    nb = fp4.buffer_sizes(N, K, pb)[2]
+    if nb:
+        wsb = torch.empty(nb, dtype=torch.uint8, device=dev)
+    nb = fp4.gemm_workspace_bytes(qa[0], qb[0])
+    if nb:
+        wsg = torch.empty(nb, dtype=torch.uint8, device=dev)
 
     # Timing events on the launch stream: one before each step's quantize and one between its
     # quantize and GEMM; a GEMM ends where the next step's first event is recorded (plus one after
@@ -141,10 +216,14 @@ def main():
         j = i % args.copies
         if ev is not None:
             ev[2 * i].record()
-        fp4.quantize_batch([xs[j], ws[j]], params, outs=[qx[j], qw[j]])
+        if wk["batched"]:
+            fp4.quantize_batch([As[j], Bs[j]], pa, outs=[qa[j], qb[j]])
+        else:
+            fp4.quantize(As[j], pa, out=qa[j], workspace=wsa)
+            fp4.quantize(Bs[j], pb, out=qb[j], workspace=wsb)
         if ev is not None:
             ev[2 * i + 1].record()
-        fp4.gemm(qx[j], qw[j], out=cs[j])
+        fp4.gemm(qa[j], qb[j], out=cs[j], workspace=wsg)
 
     for i in range(args.warmup):
         step(i)
@@ -162,8 +241,15 @@ def main():
     ms_per_step = wall / args.steps * 1e3
 
     flops = 2.0 * M * N * K
-    bytes_q = (M + N) * K * (2 + 0.5 + 1 / 32)  # bf16 in, E2M1 codes and E8M0 scales out
+
+    def qbytes(rows, p):  # bf16 in, codes and scales out
+        cb, sb, _ = fp4.buffer_sizes(rows, K, p)
+        return rows * K * 2 + cb + sb
+
+    bytes_q = qbytes(M, pa) + qbytes(N, pb)
     gemm_tflops = flops / t_g / 1e12
+    peak = FP8_PEAK_TFLOPS if wk["fp8"] else FP4_PEAK_TFLOPS
+    dtype = {False: "mxfp4", True: "mxfp8"}[wk["fp8"]] if args.workload != "nvfp4_4over6" else "nvfp4"
     out = {
         "metric": "quantize GB/s (% HBM peak); MXFP4 GEMM TFLOP/s (% FP4 MFMA peak)",
         "value": round(flops / (wall / args.steps) / 1e12, 3),
@@ -175,25 +261,26 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4",
+        "dtype": dtype,
         "data": "synthetic (seeded numpy draws of the workload's shapes and distributions)",
-        "config": {"workload": "llama7b_forward_linear", "M": M, "N": N, "K": K,
-                   "input": "bf16", "hadamard_n": HN,
-                   "quant": "E2M1 + E8M0 per 32 (floor), RNE", "output": "bf16",
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "input": "bf16",
+                   "hadamard_n": pa.hadamard_n, "quant": wk["quant"], "output": "bf16",
                    "input_copies": args.copies},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": FP4_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(),
-                     "kernel": "k_gemm_big (MXFP4, 256x256 tiles, 32x32x64 scaled MFMA, bf16 out)"},
-        "quantize_xw": {"GB/s": round(bytes_q / tq / 1e9, 1),
-                        "frac": round(bytes_q / tq / 1e9 / HBM_PEAK_GBS, 4),
-                        "us": round(tq * 1e6, 2), "bytes": int(bytes_q),
-                        "kernel": "k_segment (bf16, FWHT-128, MXFP4; X and W in one launch)"},
-        "gemm": {"TFLOP/s": round(gemm_tflops, 2), "frac": round(gemm_tflops / FP4_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
+                     "traffic": measured_traffic() if args.workload == HEADLINE else None,
+                     "kernel": wk["kernel"]},
+        "quantize": {"GB/s": round(bytes_q / tq / 1e9, 1),
+                     "frac": round(bytes_q / tq / 1e9 / HBM_PEAK_GBS, 4),
+                     "us": round(tq * 1e6, 2), "bytes": int(bytes_q),
+                     "launches": ("one batched k_segment launch for A and B" if wk["batched"]
+                                  else "separate launches for A and B")},
+        "gemm": {"TFLOP/s": round(gemm_tflops, 2), "frac": round(gemm_tflops / peak, 4),
                  "us": round(t_g * 1e6, 2), "flops": flops},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(x_bits, w_bits, args.cpu_fraction)
+        f = args.cpu_fraction if args.cpu_fraction is not None else wk["f"]
+        out["cpu_baseline"] = cpu_baseline(wk, a_bits, b_bits, pa, pb, f)
     print(json.dumps(out), flush=True)
 
 
