@@ -17,6 +17,9 @@ enum Layout { L_BAD = 0, L_SEG1D, L_SEG2D, L_ROW, L_TENSOR };
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 bool valid_hn(int n) { return n == 0 || n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
+// The segment kernels address a wave's 64 segments (up to 64 rows of a strided tensor, or the 8
+// rows of a 2D tile's slice) with 32-bit byte offsets from the tile's first row.
+bool pitch_ok(int64_t ld, int esz) { return 64 * ld * esz < (int64_t(1) << 31); }
 
 bool is_nv(int sm) {
     return sm == FP4_SCALE_NV || sm == FP4_SCALE_NV_4OVER6 || sm == FP4_SCALE_NV_GIVEN ||
@@ -124,6 +127,7 @@ int fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int
         if (lay == L_SEG1D || lay == L_SEG2D) {
             if (!aligned(x, 16) || (ldx * esz) % 16 || !aligned(codes, 16) || !aligned(scales, 8))
                 return FP4_ERR_ALIGNMENT;
+            if ((ldx != cols || lay == L_SEG2D) && !pitch_ok(ldx, esz)) return FP4_ERR_UNSUPPORTED;
         }
         const int64_t need = ws_bytes_needed(lay, p);
         if (need && (!workspace || ws_bytes < need)) return FP4_ERR_WORKSPACE;
@@ -197,6 +201,7 @@ int fp4_quantize_batch(int32_t count, const fp4_quant_item* items, int32_t x_dty
             if (sc == SC_NV && !t.tensor_scale) return FP4_ERR_INVALID_ARG;
             if (!aligned(t.x, 16) || (t.ldx * esz) % 16 || !aligned(t.codes, 16) || !aligned(t.scales, 8))
                 return FP4_ERR_ALIGNMENT;
+            if ((t.ldx != t.cols || lay == L_SEG2D) && !pitch_ok(t.ldx, esz)) return FP4_ERR_UNSUPPORTED;
             a[i].x = t.x;
             a[i].rows = t.rows;
             a[i].cols = t.cols;
@@ -326,6 +331,7 @@ int fp4_hadamard(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int
         if (!valid_hn(hadamard_n) || cols % 32 || (hadamard_n && cols % hadamard_n)) return FP4_ERR_INVALID_ARG;
         const int esz = x_dtype == FP4_DT_BF16 ? 2 : 4;
         if (!aligned(x, 16) || (ldx * esz) % 16 || !aligned(y, 16)) return FP4_ERR_ALIGNMENT;
+        if (ldx != cols && !pitch_ok(ldx, esz)) return FP4_ERR_UNSUPPORTED;
         SegArgs a{};
         a.x = x;
         a.rows = rows;

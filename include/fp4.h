@@ -129,7 +129,9 @@ int64_t fp4_workspace_bytes(int64_t rows, int64_t cols, const fp4_qparams* p);
  * v = x * RN(1/d) (d the decoded scale; exactly x / d for power-of-two scales) is rounded to the
  * element grid. Requirements: cols even for E2M1; blocks tile the tensor; 1D groups and 2D tiles
  * need cols % 32 == 0 (and rows % 32 == 0 for 2D); per-row / per-tensor blocks take no rotation;
- * SR is not combined with 4/6; x and ldx * element size 16-byte aligned; codes 16-byte aligned.
+ * SR is not combined with 4/6; x and ldx * element size 16-byte aligned; codes 16-byte aligned;
+ * a row pitch ldx != cols (and any 2D tiling) needs 64 * ldx * element size < 2^31 (32-bit
+ * offsets within a wave's tile), else FP4_ERR_UNSUPPORTED.
  * workspace: device memory of fp4_workspace_bytes() bytes (may be NULL when that is 0). */
 int fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                  const fp4_qparams* p, void* codes, void* scales, float* tensor_scale,

@@ -98,6 +98,9 @@ def test_quantize_validation_without_device(fp4):
     assert _quant(fp4, P(fp4), codes=0x2008) == E.ERR_ALIGNMENT
     assert _quant(fp4, P(fp4), ldx=260) == E.ERR_ALIGNMENT             # pitch not 16-B aligned
     assert _quant(fp4, P(fp4), ldx=100) == E.ERR_INVALID_ARG           # ldx < cols
+    assert _quant(fp4, P(fp4), ldx=1 << 24) == E.ERR_UNSUPPORTED       # 64-row tile span >= 2 GiB
+    assert _quant(fp4, P(fp4, block_rows=32), ldx=1 << 24) == E.ERR_UNSUPPORTED
+    assert fp4.lib().fp4_hadamard(0x1000, 1, 64, 256, 1 << 24, 128, 0x2000, None) == E.ERR_UNSUPPORTED
     assert _quant(fp4, P(fp4), codes=0x1000) == E.ERR_INVALID_ARG      # aliasing
 
 
