@@ -1,8 +1,11 @@
-// Block-scaled GEMM C = A * B^T on gfx950's V_MFMA_SCALE_F32_16X16X128_F8F6F4.
+// Block-scaled GEMM C = A * B^T on gfx950's scaled matrix instructions (V_MFMA_SCALE_F32_*_F8F6F4).
 //
 // Operands are K-contiguous: A [M, K] and B [N, K] as packed E2M1 (2 per byte) or E4M3 bytes,
 // with one E8M0 scale per row and 32-wide K group (B may instead carry one scale per 32 x 32
 // tile). The matrix core applies both scales itself, so the main loop is loads + MFMA only.
+// Two kernels: k_gemm_big (256 x 256 tiles, 32x32x64 MFMA, operands copied straight into LDS; the
+// path for M, N >= 256 and K a multiple of its stage depth) and k_gemm below (128 x 128 tiles,
+// 16x16x128 MFMA; every other shape).
 //
 // Lane layouts of the 16x16x128 scaled MFMA (established with one-hot probes on the hardware):
 //  - FP4: lane l supplies row l % 16 and the 32 K values [32 (l / 16), +32) as 16 contiguous

@@ -41,7 +41,9 @@ struct SegIO {
 // G = 16 / P, so that both the writes and the reads of any 16 consecutive lanes touch 16 distinct
 // slots of one 256-byte bank sweep. A wave's LDS accesses complete in order, so the read-back needs
 // no barrier.
-template <int IN>
+// With RAW, the transposition is skipped: v holds the 32 elements the lane loaded itself, from
+// several segments (enough for an order-free reduction such as the tensor amax).
+template <int IN, bool RAW = false>
 __device__ __forceinline__ void load_wave_segments(__amdgpu_buffer_rsrc_t rs, const int (&off)[SegIO<IN>::P],
                                                    u32x4* lds, float (&v)[32]) {
     constexpr int P = SegIO<IN>::P, G = 16 / P;
@@ -49,6 +51,22 @@ __device__ __forceinline__ void load_wave_segments(__amdgpu_buffer_rsrc_t rs, co
     u32x4 raw[P];
 #pragma unroll
     for (int i = 0; i < P; ++i) raw[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, 2 /* nt */);
+    if constexpr (RAW) {
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            if constexpr (IN == DT_BF16) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[8 * q + 2 * j] = bf16_lo(raw[q][j]);
+                    v[8 * q + 2 * j + 1] = bf16_hi(raw[q][j]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[4 * q + j] = __uint_as_float(raw[q][j]);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < P; ++i) {
         const int ch = 64 * i + lane, sg = ch / P, q = ch % P;
@@ -72,7 +90,7 @@ __device__ __forceinline__ void load_wave_segments(__amdgpu_buffer_rsrc_t rs, co
 
 // Loads the wave tile of 64 consecutive segments wbase .. wbase + 63 of a row-major [rows, cols]
 // tensor with row pitch ldx (segments past nseg read as zeros).
-template <int IN>
+template <int IN, bool RAW = false>
 __device__ __forceinline__ void load_wave_segments_1d(const SegArgs& a, int64_t wbase, u32x4* lds, float (&v)[32]) {
     constexpr int P = SegIO<IN>::P, ESZ = SegIO<IN>::ESZ;
     const int lane = __lane_id();
@@ -86,7 +104,7 @@ __device__ __forceinline__ void load_wave_segments_1d(const SegArgs& a, int64_t 
             (void*)(xb + wbase * 32 * ESZ), (short)0, (int)(left < 64 * 32 * ESZ ? left : 64 * 32 * ESZ), 0x00020000);
 #pragma unroll
         for (int i = 0; i < P; ++i) off[i] = 16 * (64 * i + lane);
-        load_wave_segments<IN>(rs, off, lds, v);
+        load_wave_segments<IN, RAW>(rs, off, lds, v);
     } else {
         // strided rows: per-piece offsets from the tile's first segment (row pitch below 32 MiB)
         const int64_t r0 = wbase / spr;
@@ -100,7 +118,7 @@ __device__ __forceinline__ void load_wave_segments_1d(const SegArgs& a, int64_t 
         }
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc((void*)(xb + base * ESZ), (short)0, 0x7FFFFFFF, 0x00020000);
-        load_wave_segments<IN>(rs, off, lds, v);
+        load_wave_segments<IN, RAW>(rs, off, lds, v);
     }
 }
 
@@ -296,7 +314,8 @@ __global__ __launch_bounds__(kThreads) void k_segment(SegBatch b) {
         } else {
             for (int64_t g0 = (int64_t)blockIdx.x * kThreads; g0 < a.nseg; g0 += (int64_t)gridDim.x * kThreads) {
                 float v[32];
-                load_wave_segments_1d<IN>(a, g0 + 64 * wv, stage[wv], v);
+                // without a rotation the max needs no segment order: skip the LDS transposition
+                load_wave_segments_1d<IN, HN == 0>(a, g0 + 64 * wv, stage[wv], v);
                 fwht_segment<HN>(v);
                 m = fmaxf(m, block_amax<32, 0>(v));
             }
@@ -661,7 +680,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_rowblock(DeqArgs a) {
         return hipGetLastError();                                                          \
     } while (0)
 
-// workgroups of one item of a launch (the amax pass walks the tensor with at most 1024 of them)
+// workgroups of one item of a launch (the amax pass walks the tensor with at most 512 of them)
 template <int HN, int BR>
 static int64_t seg_grid(const SegArgs& a, int pass) {
     int64_t grid;
@@ -673,7 +692,7 @@ static int64_t seg_grid(const SegArgs& a, int pass) {
     } else {
         grid = (a.rows / 32) * (((a.cols >> 5) + 7) >> 3);
     }
-    if (pass == PASS_AMAX && grid > 1024) grid = 1024;
+    if (pass == PASS_AMAX && grid > 512) grid = 512;  // two workgroups per CU: measured fastest
     return grid;
 }
 
