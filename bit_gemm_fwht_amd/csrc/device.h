@@ -199,20 +199,18 @@ __device__ __forceinline__ uint32_t e4m3_sr(float v, uint32_t u16) {
     const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
     const float a = fabsf(v);
     if (!(a < 448.0f)) return sign | 0x7Eu;
-    uint32_t lo;
-    float p;
     const uint32_t ua = __float_as_uint(a);
-    if (a >= 0.015625f) {  // normal E4M3 range: keep 3 mantissa bits
-        const uint32_t e = (ua >> 23);          // biased fp32 exponent, 121..135
-        const float glo = __uint_as_float(ua & 0xFFF00000u);
-        lo = ((e - 120u) << 3) | ((ua >> 20) & 7u);
-        p = (a - glo) * __uint_as_float((130u - (e - 127u)) << 23);  // / 2^(e-127-3)
+    uint32_t lo, up;
+    if (a >= 0.015625f) {
+        // normal E4M3 range: 3 mantissa bits kept, lo = (biased e - 120) << 3 | top 3 bits, and
+        // p * 2^16 is the 20 bits below them over 2^4 (an exact integer compare)
+        lo = (ua >> 20) - 960u;
+        up = (u16 << 4) < (ua & 0xFFFFFu) ? 1u : 0u;
     } else {  // subnormal E4M3: step 2^-9
         const float q = floorf(a * 512.0f);
         lo = (uint32_t)q;
-        p = a * 512.0f - q;
+        up = ((float)u16 < (a * 512.0f - q) * 65536.0f) ? 1u : 0u;
     }
-    const uint32_t up = ((float)u16 < p * 65536.0f) ? 1u : 0u;
     return sign | (lo + up);
 }
 
