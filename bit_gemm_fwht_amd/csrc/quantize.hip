@@ -799,7 +799,8 @@ hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t stream) {
 
 hipError_t launch_amax_rows(const void* x, int in_dtype, int64_t rows, int64_t cols, int64_t ldx,
                             uint32_t* ws, hipStream_t stream) {
-    const int64_t grid = rows < 4096 ? rows : 4096;
+    // one atomic max per workgroup on one word: more than ~512 workgroups only add contention
+    const int64_t grid = rows < 512 ? rows : 512;
     if (in_dtype == DT_BF16) BGF_LAUNCH(k_amax_rows<DT_BF16>, grid, x, rows, cols, ldx, ws);
     BGF_LAUNCH(k_amax_rows<DT_F32>, grid, x, rows, cols, ldx, ws);
 }

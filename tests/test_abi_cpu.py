@@ -98,6 +98,9 @@ def test_quantize_validation_without_device(fp4):
     assert _quant(fp4, P(fp4), codes=0x2008) == E.ERR_ALIGNMENT
     assert _quant(fp4, P(fp4), ldx=260) == E.ERR_ALIGNMENT             # pitch not 16-B aligned
     assert _quant(fp4, P(fp4), ldx=100) == E.ERR_INVALID_ARG           # ldx < cols
+    assert _quant(fp4, P(fp4), rows=0) == E.ERR_INVALID_ARG            # empty tensors are rejected
+    assert _quant(fp4, P(fp4), cols=0) == E.ERR_INVALID_ARG
+    assert _quant(fp4, P(fp4), rows=-1) == E.ERR_INVALID_ARG
     assert _quant(fp4, P(fp4), ldx=1 << 24) == E.ERR_UNSUPPORTED       # 64-row tile span >= 2 GiB
     assert _quant(fp4, P(fp4, block_rows=32), ldx=1 << 24) == E.ERR_UNSUPPORTED
     assert fp4.lib().fp4_hadamard(0x1000, 1, 64, 256, 1 << 24, 128, 0x2000, None) == E.ERR_UNSUPPORTED
@@ -154,6 +157,8 @@ def test_gemm_validation_without_device(fp4):
     assert L.fp4_gemm(ctypes.byref(a96), ctypes.byref(b96), c, 0, 128, None, None, None, 0, None) == E.ERR_UNSUPPORTED
     b8 = qt(128, 256, elem=1)
     assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(b8), c, 0, 128, None, None, None, 0, None) == E.ERR_UNSUPPORTED
+    a0 = qt(0, 256)
+    assert L.fp4_gemm(ctypes.byref(a0), ctypes.byref(b), c, 0, 128, None, None, None, 0, None) == E.ERR_INVALID_ARG
     brot = qt(128, 256, hadamard_n=128)
     assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(brot), c, 0, 128, None, None, None, 0, None) == E.ERR_INVALID_ARG
     assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(b), c, 0, 64, None, None, None, 0, None) == E.ERR_INVALID_ARG
