@@ -98,10 +98,13 @@ __device__ __forceinline__ void load_wave_segments_1d(const SegArgs& a, int64_t 
     const char* const xb = reinterpret_cast<const char*>(a.x);
     int off[P];
     if (a.ldx == a.cols) {
-        // contiguous rows: the tile is one run of bytes; the extent stops at the tensor's end
-        const int64_t left = (a.nseg - wbase) * 32 * ESZ;
+        // contiguous rows: the tile is one run of bytes; the extent stops at the tensor's end, and
+        // is 0 for a tile wholly past it (the last workgroup's trailing waves), so that nothing
+        // beyond the tensor is read
+        int64_t left = (a.nseg - wbase) * 32 * ESZ;
+        left = left < 0 ? 0 : (left < 64 * 32 * ESZ ? left : 64 * 32 * ESZ);
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(xb + wbase * 32 * ESZ), (short)0, (int)(left < 64 * 32 * ESZ ? left : 64 * 32 * ESZ), 0x00020000);
+            (void*)(xb + (left > 0 ? wbase * 32 * ESZ : 0)), (short)0, (int)left, 0x00020000);
 #pragma unroll
         for (int i = 0; i < P; ++i) off[i] = 16 * (64 * i + lane);
         load_wave_segments<IN, RAW>(rs, off, lds, v);

@@ -395,6 +395,25 @@ def test_gemm_fused_output_quantize_rotated(orc, M, N, K, kind, hns):
             assert torch.equal(cq2.codes, cq.codes) and torch.equal(cq2.scales, cq.scales)
 
 
+@pytest.mark.parametrize("rows,cols,hn", [(107, 128, 32), (107, 128, 64), (86, 32, 0), (3, 256, 128)])
+def test_tensor_amax_ignores_memory_past_the_tensor(orc, rows, cols, hn):
+    """Regression: the last workgroup's trailing waves (segment count not a multiple of 256) must
+    read nothing past the tensor. The tensor is the head of a larger buffer whose tail holds 1e30,
+    so any read past its end would show up in the NVFP4 tensor scale and the codes."""
+    rng = np.random.default_rng(rows + cols + hn)
+    x = (rng.standard_normal((rows, cols)) * 3).astype(np.float32)
+    big = torch.full((rows + 256, cols), 1e30, dtype=torch.float32, device=DEV)
+    big[:rows] = torch.from_numpy(x).to(DEV)
+    for sm in (NV, NV46):
+        p = P(block=(1, 16), scale_mode=sm, hadamard_n=hn)
+        q = fp4.quantize(big[:rows], p)
+        torch.cuda.synchronize()
+        oc, os_, ot = _orc_quant(orc, x, p)
+        assert q.tensor_scale.cpu().numpy().view(np.uint32)[0] == ot.view(np.uint32)[0]
+        assert np.array_equal(q.codes.cpu().numpy(), oc.reshape(-1))
+        assert np.array_equal(q.scales.cpu().numpy(), os_.reshape(-1).view(np.uint8))
+
+
 BATCH_CASES = [
     # dtype, shapes, params
     ("bf16", [(4096 // 16, 4096 // 8), (11008 // 43, 4096 // 8)], dict(hadamard_n=128)),
