@@ -11,11 +11,14 @@ import torch
 
 from bit_gemm_fwht_amd import fp4
 from bit_gemm_fwht_amd import workloads as wl
-from test_gpu_parity import (CEIL, E2M1, E4M3, F32, FLOOR, NV, NV46, RNE, SR, P, _check_quant, _gemm_check)
+from test_gpu_parity import (CEIL, E2M1, E4M3, F32, FLOOR, NV, NV46, RNE, SR, P, _check_quant, _gemm_check,
+                             _orc_quant, _to_dev)
+
+DEV = "cuda:0"
 
 pytestmark = pytest.mark.gpu
 
-N_QUANT, N_GEMM = 24, 16
+N_QUANT, N_GEMM, N_EXTRA = 40, 24, 16
 
 
 def _quant_case(seed):
@@ -77,3 +80,75 @@ def test_random_gemm(orc, seed):
     A = (rng.standard_normal((M, K)) * 10.0 ** rng.uniform(-2, 2)).astype(np.float32)
     B = (rng.standard_normal((N, K)) * 10.0 ** rng.uniform(-3, 1)).astype(np.float32)
     _gemm_check(orc, A, B, pa, pb, c_dtype=c_dtype)
+
+
+def _input(rng, rows, cols, dtype):
+    x = (rng.standard_normal((rows, cols)) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32)
+    x[rng.random((rows, cols)) < 0.01] *= 40.0
+    return wl.f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def _same(q, oc, os_, what):
+    assert np.array_equal(q.codes.cpu().numpy(), oc.reshape(-1)), f"{what}: codes differ from the oracle"
+    assert np.array_equal(q.scales.cpu().numpy(), os_.reshape(-1).view(np.uint8)), f"{what}: scales differ"
+
+
+@pytest.mark.parametrize("seed", range(N_EXTRA))
+def test_random_strided_colwise_batch(orc, seed):
+    """A 1D mode from the quantize draw, applied three more ways: with a row pitch wider than the
+    row, column-wise (x^T without forming it), and in a batch with a second tensor."""
+    rows, cols, dtype, params = _quant_case(100 + seed)
+    if params.block[0] != 1:
+        params = P(elem=params.elem, block=(1, 32), scale_mode=CEIL, round_mode=params.round_mode,
+                   hadamard_n=params.hadamard_n, seed=params.seed)
+    rng = np.random.default_rng(500 + seed)
+    x = _input(rng, rows, cols, dtype)
+    oc, os_, ot = _orc_quant(orc, x, params)
+    # strided rows: x is the left part of a wider buffer
+    xd = _to_dev(x)
+    wide = torch.zeros(rows, cols + 32 * int(rng.integers(1, 4)), dtype=xd.dtype, device=DEV)
+    wide[:, :cols] = xd
+    q = fp4.quantize(wide[:, :cols], params)
+    torch.cuda.synchronize()
+    _same(q, oc, os_, "strided")
+    # column-wise: quantize y^T for y = xc^T, xc the first r8 rows of x (y's row count, cols, a
+    # multiple of 32; its row pitch, r8 elements, a multiple of 16 bytes)
+    r8 = rows // 8 * 8
+    if cols % 32 == 0 and r8 >= 8:
+        xc = np.ascontiguousarray(x[:r8])
+        occ, osc, _ = _orc_quant(orc, xc, params)
+        qc = fp4.quantize_colwise(_to_dev(np.ascontiguousarray(xc.T)), params)
+        torch.cuda.synchronize()
+        _same(qc, occ, osc, "colwise")
+    # batched with a second tensor of another shape (modes without a tensor-wide amax)
+    if params.scale_mode not in (NV, NV46):
+        rows2 = int(rng.integers(1, 200))
+        x2 = _input(rng, rows2, cols, dtype)
+        oc2, os2, _ = _orc_quant(orc, x2, params)
+        q1, q2 = fp4.quantize_batch([_to_dev(x), _to_dev(x2)], params)
+        torch.cuda.synchronize()
+        _same(q1, oc, os_, "batch item 0")
+        _same(q2, oc2, os2, "batch item 1")
+
+
+@pytest.mark.parametrize("seed", range(N_EXTRA))
+def test_random_fused_output_quantize(orc, seed):
+    """Random GEMM shape and operand kind with a random fused output quantize (element, scale
+    rule, rounding, rotation along N): codes and scales equal the oracle's quantization of the
+    fp32 C the same call stores."""
+    M, N, K, pa, pb, _ = _gemm_case(300 + seed)
+    rng = np.random.default_rng(700 + seed)
+    hns = [h for h in (0, 16, 32, 64, 128) if h == 0 or N % h == 0]
+    oq = P(elem=E4M3 if rng.random() < 0.3 else E2M1, scale_mode=CEIL if rng.random() < 0.5 else FLOOR,
+           round_mode=SR if rng.random() < 0.4 else RNE, hadamard_n=int(rng.choice(hns)),
+           seed=int(rng.integers(0, 2**40)))
+    A = (rng.standard_normal((M, K))).astype(np.float32)
+    B = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    ca, sa, ta = _orc_quant(orc, A, pa)
+    cb, sb, tb = _orc_quant(orc, B, pb)
+    qa = fp4.upload_qtensor(ca, sa, ta, M, K, pa, DEV)
+    qb = fp4.upload_qtensor(cb, sb, tb, N, K, pb, DEV)
+    c, cq = fp4.gemm(qa, qb, out_dtype=torch.float32, out_q=oq)
+    torch.cuda.synchronize()
+    oc, os_, _ = _orc_quant(orc, c.cpu().numpy(), oq)
+    _same(cq, oc, os_, f"fused out_q {oq}")
