@@ -151,7 +151,9 @@ def buffer_sizes(rows: int, cols: int, params: Params) -> tuple[int, int, int]:
     sb = L.fp4_scales_bytes(rows, cols, ctypes.byref(p))
     wb = L.fp4_workspace_bytes(rows, cols, ctypes.byref(p))
     if cb < 0 or sb < 0 or wb < 0:
-        raise Fp4Error(ERR_INVALID_ARG, f"quantize params {params} for shape ({rows}, {cols})")
+        # the size queries return -1 for anything fp4_quantize would reject, invalid or unsupported
+        raise Fp4Error(ERR_INVALID_ARG, f"quantize params {params} for shape ({rows}, {cols}) are rejected "
+                       "(invalid, or not supported: e.g. 1D groups need cols % 32 == 0)")
     return cb, sb, wb
 
 
