@@ -27,7 +27,10 @@
  *  - Every argument is validated on the host before anything is queued. On any error nothing is
  *    queued and the outputs are left untouched. A launch failure returns FP4_ERR_HIP; a device
  *    fault surfaces at the caller's next synchronisation. No C++ exception crosses this ABI.
- *  - Non-finite inputs are outside the contract: kernels do not fault, results are unspecified.
+ *  - Non-finite inputs are outside the contract: kernels do not fault, results are unspecified. So
+ *    are finite inputs whose rotation overflows fp32 in an intermediate butterfly stage (max |x|
+ *    near 2^128 / n for hadamard_n = n): the overflowed values become inf / NaN, whose payloads and
+ *    ordering are not reproduced bit for bit.
  *
  * Layouts:
  *  - x / y: row-major [rows, cols] with leading dimension ld (elements), fp32 or bf16.
