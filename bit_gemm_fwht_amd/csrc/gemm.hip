@@ -83,7 +83,11 @@ __device__ __forceinline__ void small_gload(const uint8_t* a, const uint8_t* b, 
 // [M, N/2] (E2M1) or [M, N] (E4M3) bytes, scales [M, N/32]. The C tile is staged in LDS so that
 // one lane holds one group and the groups of a row sit in consecutive lanes.
 // ---------------------------------------------------------------------------------------------
-template <bool FP8, bool B2D, int OUT, bool NVG, bool FQ>
+// FQ: fused output quantize, 0 none, FQ_RNE or FQ_SR (a template argument, so that the nearest-even
+// variant carries no stochastic-rounding registers)
+constexpr int FQ_NONE = 0, FQ_RNE = 1, FQ_SR = 2;
+
+template <bool FP8, bool B2D, int OUT, bool NVG, int FQ>
 __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
     using C = Cfg<FP8>;
     // operand slabs; the fused output quantize reuses them to stage 32 rows of C at a time
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
     // epilogue: lane holds C[m][n .. n+3]
     float gscale = 1.0f;
     if constexpr (NVG) gscale = (*g.ga) * (*g.gb);
-    if constexpr (FQ) {
+    if constexpr (FQ != FQ_NONE) {
         // fused output quantization (the rules of the big kernel's epilogue): four rounds of 32
         // rows; the two waves holding a round's rows stage their fp32 values in LDS, then one
         // thread per 32-column group (the four groups of a row in consecutive lanes) reads its
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
                 uint32_t rw[16], out[8];
                 const float amax = block_amax<32, 0>(v);
                 uint32_t sbyte;
-                if (g.q_round == RND_SR) {
+                if constexpr (FQ == FQ_SR) {
                     philox_segment(g.q_seed, (uint64_t)(m * g.N + nb), rw);
                     sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, rw, out)
                                                   : e8m0_block<ELEM_E4M3, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, rw, out);
@@ -321,7 +325,7 @@ __device__ __forceinline__ void wait_lgkm0() {
     __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
 }
 
-template <bool FP8, bool B2D, int OUT, bool NVG, bool FQ>
+template <bool FP8, bool B2D, int OUT, bool NVG, int FQ>
 __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
     using C = Big<FP8>;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -547,7 +551,7 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
     const int64_t me0 = m0 + opaque_zero, ne0 = n0 + opaque_zero, ldc = g.ldc + opaque_zero;
     char* const cbase = reinterpret_cast<char*>(g.c) + opaque_zero;
     const int64_t Mx = g.M + opaque_zero, Nx = g.N + opaque_zero;
-    if constexpr (FQ) {
+    if constexpr (FQ != FQ_NONE) {
         // fused output quantization, in two passes of 128 columns: the fp32 values (as an fp32 C
         // would hold them) are staged in LDS, [256 rows][128] per pass (pass p holds tile columns
         // [128 p, 128 p + 128), written by the four waves with wn / 2 = p), then one thread per
@@ -588,7 +592,7 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
                 uint32_t rw[16], out[8];
                 const float amax = block_amax<32, 0>(v);
                 uint32_t sbyte;
-                if (g.q_round == RND_SR) {
+                if constexpr (FQ == FQ_SR) {
                     philox_segment(g.q_seed, (uint64_t)(m * Nx + nb), rw);
                     sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, rw, out)
                                                   : e8m0_block<ELEM_E4M3, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, rw, out);
@@ -737,7 +741,7 @@ __global__ __launch_bounds__(256) void k_nv_to_fp8(const uint8_t* codes, const u
     dst[1] = (u32x4){o[4], o[5], o[6], o[7]};
 }
 
-template <bool FP8, bool B2D, bool NVG, bool FQ>
+template <bool FP8, bool B2D, bool NVG, int FQ>
 static hipError_t launch_out(const GemmArgs& g, int c_dtype, hipStream_t s) {
     const int64_t rowb = FP8 ? g.K : g.K / 2;
     if (g.M >= 256 && g.N >= 256 && g.K % Big<FP8>::KSTEP == 0 && g.M * rowb < (1ll << 31) &&
@@ -764,7 +768,7 @@ static hipError_t launch_out(const GemmArgs& g, int c_dtype, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <bool FQ>
+template <int FQ>
 static hipError_t launch_kind(const GemmArgs& g, int kind, int c_dtype, hipStream_t s) {
     if (kind == 0) {
         if (g.b_2d) return launch_out<false, true, false, FQ>(g, c_dtype, s);
@@ -788,8 +792,11 @@ static hipError_t launch_kind(const GemmArgs& g, int kind, int c_dtype, hipStrea
 }
 
 hipError_t launch_gemm(const GemmArgs& g, int kind, int c_dtype, int fused_q, hipStream_t s) {
-    if (fused_q) return launch_kind<true>(g, kind, c_dtype, s);
-    return launch_kind<false>(g, kind, c_dtype, s);
+    if (fused_q) {
+        if (g.q_round == RND_SR) return launch_kind<FQ_SR>(g, kind, c_dtype, s);
+        return launch_kind<FQ_RNE>(g, kind, c_dtype, s);
+    }
+    return launch_kind<FQ_NONE>(g, kind, c_dtype, s);
 }
 
 }  // namespace bgf
