@@ -1,0 +1,98 @@
+"""CPU checks of the benchmark's host logic and of the synthetic workload recipes: one GPU only,
+every workload's quantization is accepted by the library's size queries, the traffic summary is
+read only when its recorded kernel hash matches, and the generators draw the stated shapes,
+outlier counts and distributions."""
+import hashlib
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from bit_gemm_fwht_amd import workloads as wl  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def fp4():
+    from bit_gemm_fwht_amd import fp4 as m
+    if not os.path.exists(m.LIB_PATH):
+        from bit_gemm_fwht_amd import build
+        build.build()
+    m.lib()
+    return m
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+@pytest.mark.parametrize("name", sorted(bench.WORKLOADS))
+def test_workload_quantization_is_valid(fp4, name):
+    wk = bench.WORKLOADS[name]
+    for side, rows in (("a", wk["M"]), ("b", wk["N"])):
+        p = bench.params_of(fp4, wk[side])
+        codes, scales, _ = fp4.buffer_sizes(rows, wk["K"], p)
+        per = 1 if p.elem == fp4.E4M3 else 0.5
+        assert codes == int(rows * wk["K"] * per)
+        assert scales > 0
+    assert wk["fp8"] == (bench.params_of(fp4, wk["a"]).elem == fp4.E4M3 or name == "nvfp4_4over6")
+
+
+def test_traffic_summary_is_read_only_for_the_current_kernel(tmp_path, monkeypatch):
+    src = hashlib.sha256(open(bench.GEMM_SRC, "rb").read()).hexdigest()
+    f = tmp_path / "summary.md"
+    f.write_text(f"kernel source sha256: {src}\ncalibrated bytes per launch: 123456789\n")
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(f))
+    assert bench.measured_traffic() == 123456789
+    f.write_text(f"kernel source sha256: {'0' * 64}\ncalibrated bytes per launch: 123456789\n")
+    assert bench.measured_traffic() is None
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(tmp_path / "missing.md"))
+    assert bench.measured_traffic() is None
+
+
+def test_committed_traffic_summary_format():
+    text = open(bench.TRAFFIC_SUMMARY).read()
+    assert "kernel source sha256:" in text and "calibrated bytes per launch:" in text
+    assert "rocprofv3" in text  # the command that produced it
+
+
+def test_llama_linear_recipe():
+    x, w, ch = wl.llama_linear(0, m=512, n=384, k=4096)
+    assert x.shape == (512, 4096) and w.shape == (384, 4096) and x.dtype == np.uint16
+    assert len(ch) == 41 and len(np.unique(ch)) == 41  # 1 % of 4096 channels
+    xf, wf = wl.bf16_bits_to_f32(x), wl.bf16_bits_to_f32(w)
+    others = np.setdiff1d(np.arange(4096), ch)
+    s_out, s_in = xf[:, ch].std(), xf[:, others].std()
+    assert 18.0 < s_out / s_in < 22.0
+    assert abs(wf.std() - 0.02) < 0.0005 and abs(wf.mean()) < 0.0005
+    # seeded: the same draw twice
+    x2, _, ch2 = wl.llama_linear(0, m=512, n=384, k=4096)
+    assert np.array_equal(x, x2) and np.array_equal(ch, ch2)
+
+
+def test_backward_2d_recipe():
+    w, dy = wl.backward_2d(0, m=1024, n=512, k=4096)
+    assert w.shape == (512, 4096) and dy.shape == (1024, 4096)
+    d = wl.bf16_bits_to_f32(dy).astype(np.float64) / 1e-3
+    # Student-t(3): median |t| = 0.765, heavy tails (kurtosis far above the normal's 3)
+    assert abs(np.median(np.abs(d)) - 0.765) < 0.02
+    assert np.mean(np.abs(d) > 10) > 1e-3
+
+
+def test_nvfp4_4over6_recipe():
+    x, w = wl.nvfp4_4over6(0, m=1024, n=256, k=1024)
+    assert x.shape == (1024, 1024) and w.shape == (256, 1024)
+    xf = np.abs(wl.bf16_bits_to_f32(x).astype(np.float64))
+    # Laplace(0, 1) with 0.1 % of entries (1049 of 1024^2) scaled x30: an unscaled draw exceeds 30
+    # with probability e^-30, a scaled one with probability e^-1, so about 1049 / e = 386 do
+    assert 300 < np.sum(xf > 30.0) < 480
+    assert abs(np.median(xf) - np.log(2.0)) < 0.02
