@@ -13,12 +13,16 @@ forward linear:
   nvfp4_4over6       8192^3: X Laplace with 0.1% x30 outliers, W N(0, 0.02^2), NVFP4 with the
                      4/6 choice (tensor amax pass + quantize), GEMM through the FP8 re-expression
 Inputs are resident in HBM before timing starts; the step cycles over several copies of the inputs
-(more than the 256 MB last-level cache) so that every step reads its inputs from HBM.
+(more than the 256 MB last-level cache) so that every step reads its inputs from HBM. Before the
+warm-up steps the step runs untimed for --settle seconds (0.3 s), the time the GPU takes to reach
+the steady clocks of sustained work.
 
 Prints one JSON line. `value` is the step's effective throughput in TFLOP/s (GEMM FLOPs over the
 whole step time, quantization included); the per-kernel GB/s / TFLOP/s and roofline fractions are
 in the extra fields. `roofline` is the dominant kernel (the GEMM): algorithmic FLOPs per launch over
-its average launch time from HIP events on the launch stream; its `traffic` is the measured memory
+its average launch time from HIP events on the launch stream (created with
+hipEventDisableSystemFence, so that recording them does not flush the caches between the kernels
+they bracket); its `traffic` is the measured memory
 traffic per launch from the committed counter summary (headline workload only), reported only while
 the summary's kernel source hash matches the current source. `cpu_baseline` times the CPU oracle on
 a bounded sample of the same step.
@@ -76,6 +80,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--copies", type=int, default=4, help="input copies cycled through (> LLC)")
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed steps before the warm-up steps (clock ramp-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-fraction", type=float, default=None,
                     help="fraction f of A rows and B rows the CPU oracle processes")
@@ -119,6 +125,61 @@ def measured_traffic():
     if not m_src or not m_b or m_src.group(1) != src:
         return None
     return int(m_b.group(1))
+
+
+class HipTimingEvent:
+    """A HIP event for timing, created with hipEventDisableSystemFence: recording it writes a
+    timestamp on the stream without the system-scope cache write-back and invalidation that a
+    default event (and so torch.cuda.Event) performs, which slows the kernel that follows it and
+    adds several microseconds to every interval. Recorded on the stream the library launches on."""
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            # the HIP runtime torch has loaded (one runtime per process)
+            path = "libamdhip64.so"
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    if "libamdhip64" in line:
+                        path = line.split()[-1]
+                        break
+            h = ctypes.CDLL(path)
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self, stream_handle):
+        import ctypes
+        self._c = ctypes
+        self.stream = ctypes.c_void_p(stream_handle)
+        self.h = ctypes.c_void_p()
+        rc = self._lib().hipEventCreateWithFlags(ctypes.byref(self.h), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self):
+        rc = self._lib().hipEventRecord(self.h, self.stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both recorded and complete)."""
+        f = self._c.c_float()
+        rc = self._lib().hipEventElapsedTime(self._c.byref(f), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return f.value
+
+    def __del__(self):
+        if self._hip is not None and self.h:
+            self._hip.hipEventDestroy(self.h)
 
 
 def copy_calibration(mib):
@@ -225,10 +286,21 @@ def main():
             ev[2 * i + 1].record()
         fp4.gemm(qa[j], qb[j], out=cs[j], workspace=wsg)
 
+    # The GPU's clocks ramp up over the first tens of milliseconds of sustained work (a step runs
+    # ~15 % slower at first): run the step untimed for --settle seconds before the warm-up steps,
+    # so that the timed steps see the steady state a continuously busy GPU runs at.
+    t_settle = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(20):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    evs = [HipTimingEvent(stream) for _ in range(2 * args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):

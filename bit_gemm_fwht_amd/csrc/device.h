@@ -1,4 +1,4 @@
-// Device-side building blocks for gfx950 (CDNA4): bf16 unpacking, DPP lane exchange, the
+// Device-side building blocks for gfx950 (CDNA4): bf16 unpacking, lane exchange, the
 // hardware scaled converts to FP4 / FP8, Philox4x32-10, and the scale rules.
 //
 // Everything here is computed in fp32 with IEEE round-to-nearest-even per operation; the library
@@ -38,24 +38,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// DPP lane exchange within a row of 16 lanes
+// Lane exchange through the LDS crossbar (ds_swizzle, bit mode: lane l of each 32-lane half reads
+// lane ((l & and) | or) ^ xor of the same half; no LDS memory is touched). It runs on the LDS
+// pipeline rather than as a VALU instruction: measured on the rotate + quantize, the butterfly
+// stages across lanes cost 2.7 us (H_128) and 4.3 us (H_256) less over the Llama-7B X and W than
+// with DPP moves, which take a VALU slot each (two for l ^ 4), next to the butterfly's own.
 // ---------------------------------------------------------------------------------------------
-constexpr int dpp_quad(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
-constexpr int DPP_ROW_HALF_MIRROR = 0x141;
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// value of lane (lane ^ M), M in {1, 2, 4}
+// value of lane (lane ^ M), M in {1, 2, 4, 8, 16}
 template <int M>
 __device__ __forceinline__ float lane_xor(float v) {
-    if constexpr (M == 1) return dpp_mov<dpp_quad(1, 0, 3, 2)>(v);
-    if constexpr (M == 2) return dpp_mov<dpp_quad(2, 3, 0, 1)>(v);
-    // xor 4 = mirror within 8 lanes (i -> 7 - i), then reverse within 4 (i -> 3 - i)
-    if constexpr (M == 4) return dpp_mov<dpp_quad(3, 2, 1, 0)>(dpp_mov<DPP_ROW_HALF_MIRROR>(v));
-    return v;
+    static_assert(M >= 1 && M <= 16 && (M & (M - 1)) == 0, "xor within a 32-lane half");
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (M << 10) | 0x1F));
 }
 
 // 1 / sqrt(n) rounded to the nearest fp32, for the Hadamard normalisation

@@ -5,7 +5,7 @@
 // 16-element NVFP4 block half a lane, and a Hadamard chunk of n elements n/32 adjacent lanes:
 //  - n <= 32: all butterfly stages run inside the lane's registers;
 //  - n = 64, 128, 256: stages h = 1..16 run in registers, then h = 32, 64, 128 pair lane l with
-//    lane l ^ 1, ^ 2, ^ 4 through DPP (quad permutes; ^4 as half-row mirror + quad reverse).
+//    lane l ^ 1, ^ 2, ^ 4 through the LDS crossbar (ds_swizzle).
 // Each stage computes partner + (+-1) * self in one fused multiply-add, which equals the
 // butterfly's sum / difference exactly, in the same stage order as the definition (h ascending,
 // then one multiply by RN(1/sqrt(n))), so rotated values are bit-identical to that order.
