@@ -167,44 +167,35 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
 // p = (|v| - lo) / (hi - lo) (exact: the gap is a power of two). Saturates at the grid maximum.
 // Returns the code (sign bit 3 for E2M1, bit 7 for E4M3).
 // ---------------------------------------------------------------------------------------------
+// Both are branch-free: every lane evaluates the same instructions (the data-dependent branches of
+// a per-range formulation diverge within a wave on any real tensor).
 __device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t u16) {
-    const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
     const float a = fabsf(v);
-    if (!(a < 6.0f)) return sign | 7u;
-    uint32_t lo;
-    float p;
-    if (a >= 1.0f) {
-        // a in [1, 6): grid spacing within binade e (0, 1, 2) is 2^(e-1); lo keeps 1 mantissa bit
-        const uint32_t ua = __float_as_uint(a);
-        const uint32_t e = (ua >> 23) - 127u;
-        const float glo = __uint_as_float(ua & 0xFFC00000u);
-        lo = 2u + 2u * e + ((ua >> 22) & 1u);
-        p = (a - glo) * __uint_as_float((128u - e) << 23);  // / 2^(e-1)
-    } else {
-        lo = a >= 0.5f ? 1u : 0u;
-        p = (a - 0.5f * (float)lo) * 2.0f;
-    }
+    // grid spacing 2^(e-1): e = 0 on [0, 2) (0, 0.5, 1, 1.5), 1 on [2, 4) (2, 3), 2 from 4 (4, 6)
+    const int e = min(max((int)(__float_as_uint(a) >> 23) - 127, 0), 2);
+    const float q = a * __uint_as_float((uint32_t)(128 - e) << 23);  // |v| in grid steps, exact
+    const float fl = floorf(q);                                      // lo's position (exact)
+    const float p = q - fl;                                          // exact, in [0, 1)
     const uint32_t up = ((float)u16 < p * 65536.0f) ? 1u : 0u;
-    return sign | (lo + up);
+    // codes: position fl on [0, 2) is code fl; on [2, 4) and [4, 6) code fl + 2 e
+    const uint32_t code = a < 6.0f ? (uint32_t)fl + 2u * (uint32_t)e + up : 7u;
+    return ((__float_as_uint(v) >> 28) & 8u) | code;
 }
 
 __device__ __forceinline__ uint32_t e4m3_sr(float v, uint32_t u16) {
-    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
     const float a = fabsf(v);
-    if (!(a < 448.0f)) return sign | 0x7Eu;
     const uint32_t ua = __float_as_uint(a);
-    uint32_t lo, up;
-    if (a >= 0.015625f) {
-        // normal E4M3 range: 3 mantissa bits kept, lo = (biased e - 120) << 3 | top 3 bits, and
-        // p * 2^16 is the 20 bits below them over 2^4 (an exact integer compare)
-        lo = (ua >> 20) - 960u;
-        up = (u16 << 4) < (ua & 0xFFFFFu) ? 1u : 0u;
-    } else {  // subnormal E4M3: step 2^-9
-        const float q = floorf(a * 512.0f);
-        lo = (uint32_t)q;
-        up = ((float)u16 < (a * 512.0f - q) * 65536.0f) ? 1u : 0u;
-    }
-    return sign | (lo + up);
+    // normal E4M3 range (a >= 2^-6): 3 mantissa bits kept, lo = (biased e - 120) << 3 | top 3
+    // bits, and p * 2^16 is the 20 bits below them over 2^4 (an exact integer compare)
+    const uint32_t lo_n = (ua >> 20) - 960u;
+    const uint32_t up_n = (u16 << 4) < (ua & 0xFFFFFu) ? 1u : 0u;
+    // subnormal E4M3 (a < 2^-6): step 2^-9
+    const float s = a * 512.0f;
+    const float q = floorf(s);
+    const uint32_t up_s = ((float)u16 < (s - q) * 65536.0f) ? 1u : 0u;
+    uint32_t code = a >= 0.015625f ? lo_n + up_n : (uint32_t)q + up_s;
+    code = a < 448.0f ? code : 0x7Eu;
+    return ((__float_as_uint(v) >> 24) & 0x80u) | code;
 }
 
 }  // namespace bgf
