@@ -59,8 +59,8 @@ def lib() -> ctypes.CDLL:
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
-                          "g.build()'` (hipcc, gfx950)")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python bit_gemm_fwht_amd/build.py` "
+                          "(hipcc, gfx950)")
     L = ctypes.CDLL(LIB_PATH)
     P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     QP = ctypes.POINTER(QParams)
