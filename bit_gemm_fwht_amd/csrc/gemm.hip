@@ -199,16 +199,16 @@ __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
                     for (int i = 0; i < 4; ++i) v[4 * c + i] = x[i];
                 }
                 fwht_groups(v, g.q_hn);
-                uint32_t rw[16], out[8];
+                uint32_t out[8];
                 const float amax = block_amax<32, 0>(v);
                 uint32_t sbyte;
+                const SrSource sr{g.q_seed, (uint64_t)(m * g.N + nb)};
                 if constexpr (FQ == FQ_SR) {
-                    philox_segment(g.q_seed, (uint64_t)(m * g.N + nb), rw);
-                    sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, rw, out)
-                                                  : e8m0_block<ELEM_E4M3, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, rw, out);
+                    sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, sr, out)
+                                                  : e8m0_block<ELEM_E4M3, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, sr, out);
                 } else {
-                    sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_RNE, 32, 0>(v, amax, g.q_ceil != 0, rw, out)
-                                                  : e8m0_block<ELEM_E4M3, RND_RNE, 32, 0>(v, amax, g.q_ceil != 0, rw, out);
+                    sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_RNE, 32, 0>(v, amax, g.q_ceil != 0, sr, out)
+                                                  : e8m0_block<ELEM_E4M3, RND_RNE, 32, 0>(v, amax, g.q_ceil != 0, sr, out);
                 }
                 if (m < g.M && nb < g.N) {
                     if (g.q_elem == ELEM_E2M1) {
@@ -589,16 +589,16 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
                     for (int i = 0; i < 4; ++i) v[4 * c + i] = x[i];
                 }
                 fwht_groups(v, g.q_hn);
-                uint32_t rw[16], out[8];
+                uint32_t out[8];
                 const float amax = block_amax<32, 0>(v);
                 uint32_t sbyte;
+                const SrSource sr{g.q_seed, (uint64_t)(m * Nx + nb)};
                 if constexpr (FQ == FQ_SR) {
-                    philox_segment(g.q_seed, (uint64_t)(m * Nx + nb), rw);
-                    sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, rw, out)
-                                                  : e8m0_block<ELEM_E4M3, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, rw, out);
+                    sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, sr, out)
+                                                  : e8m0_block<ELEM_E4M3, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, sr, out);
                 } else {
-                    sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_RNE, 32, 0>(v, amax, g.q_ceil != 0, rw, out)
-                                                  : e8m0_block<ELEM_E4M3, RND_RNE, 32, 0>(v, amax, g.q_ceil != 0, rw, out);
+                    sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_RNE, 32, 0>(v, amax, g.q_ceil != 0, sr, out)
+                                                  : e8m0_block<ELEM_E4M3, RND_RNE, 32, 0>(v, amax, g.q_ceil != 0, sr, out);
                 }
                 if (m < Mx && nb < Nx) {
                     if (g.q_elem == ELEM_E2M1) {

@@ -16,23 +16,27 @@ __device__ __forceinline__ float block_amax(const float (&v)[32]) {
     return m;
 }
 
-// Philox words for elements idx0 .. idx0 + 31 (idx0 a multiple of 32): u16 for element j is the
-// low (even j) / high (odd j) half of word (j >> 1) & 3 of the call for counter (idx0 + j) >> 3.
-__device__ __forceinline__ void philox_segment(uint64_t seed, uint64_t idx0, uint32_t (&w)[16]) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const uint64_t ctr = (idx0 >> 3) + (uint64_t)g;
-        uint32_t c0 = (uint32_t)ctr, c1 = (uint32_t)(ctr >> 32), c2 = 0u, c3 = 0u;
-        philox4x32_10(c0, c1, c2, c3, (uint32_t)seed, (uint32_t)(seed >> 32));
-        w[4 * g + 0] = c0;
-        w[4 * g + 1] = c1;
-        w[4 * g + 2] = c2;
-        w[4 * g + 3] = c3;
-    }
+// Random source of stochastic rounding for the segment of elements idx0 .. idx0 + 31 (idx0 a
+// multiple of 32): u16 for element idx is the low (even idx) / high (odd idx) half of word
+// (idx >> 1) & 3 of the Philox4x32-10 call for counter idx >> 3 and key seed. The words are
+// generated where they are used, one call per 8 elements, so that only four are live at a time.
+struct SrSource {
+    uint64_t seed, idx0;
+};
+
+// the four words of group g8 (elements 8 g8 .. 8 g8 + 7 of the segment)
+__device__ __forceinline__ void philox_group(const SrSource& sr, int g8, uint32_t (&c)[4]) {
+    const uint64_t ctr = (sr.idx0 >> 3) + (uint64_t)g8;
+    c[0] = (uint32_t)ctr;
+    c[1] = (uint32_t)(ctr >> 32);
+    c[2] = 0u;
+    c[3] = 0u;
+    philox4x32_10(c[0], c[1], c[2], c[3], (uint32_t)sr.seed, (uint32_t)(sr.seed >> 32));
 }
-__device__ __forceinline__ uint32_t sr_u16(const uint32_t (&w)[16], int j) {
-    const uint32_t word = w[j >> 1];
-    return (j & 1) ? (word >> 16) : (word & 0xFFFFu);
+// u16 of element e (0..7) of a group
+__device__ __forceinline__ uint32_t sr_u16(const uint32_t (&c)[4], int e) {
+    const uint32_t word = c[e >> 1];
+    return (e & 1) ? (word >> 16) : (word & 0xFFFFu);
 }
 
 // Blockwise H_n / sqrt(n) along a row for n in {0, 16, 32, 64, 128} chosen at run time (the same
@@ -79,7 +83,7 @@ __device__ __forceinline__ void fwht_groups(float (&v)[32], int n) {
 //  else: elements are v * rcp (RN), converted with scale 1.
 template <int ELEM, int RND, int B, int OFF>
 __device__ __forceinline__ void encode_block(float (&v)[32], bool pow2, float cvt_scale, float rcp,
-                                             float clampv, const uint32_t (&rw)[16],
+                                             float clampv, const SrSource& sr,
                                              uint32_t (&out)[8]) {
     if constexpr (RND == RND_RNE) {
         if (!pow2) {
@@ -114,20 +118,30 @@ __device__ __forceinline__ void encode_block(float (&v)[32], bool pow2, float cv
 #pragma unroll
         for (int i = OFF; i < OFF + B; ++i) v[i] = v[i] * rcp;
         if constexpr (ELEM == ELEM_E2M1) {
+            // word w of out holds the 8 nibbles of group w
 #pragma unroll
             for (int w = OFF / 8; w < (OFF + B) / 8; ++w) {
+                uint32_t c[4];
+                philox_group(sr, w, c);
                 uint32_t r = 0u;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) r |= e2m1_sr(v[8 * w + j], sr_u16(rw, 8 * w + j)) << (4 * j);
+                for (int j = 0; j < 8; ++j) r |= e2m1_sr(v[8 * w + j], sr_u16(c, j)) << (4 * j);
                 out[w] = r;
             }
         } else {
+            // words 2 g8 and 2 g8 + 1 of out hold the 8 bytes of group g8
 #pragma unroll
-            for (int w = OFF / 4; w < (OFF + B) / 4; ++w) {
-                uint32_t r = 0u;
+            for (int g8 = OFF / 8; g8 < (OFF + B) / 8; ++g8) {
+                uint32_t c[4];
+                philox_group(sr, g8, c);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) r |= e4m3_sr(v[4 * w + j], sr_u16(rw, 4 * w + j)) << (8 * j);
-                out[w] = r;
+                for (int h = 0; h < 2; ++h) {
+                    const int w = 2 * g8 + h;
+                    uint32_t r = 0u;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) r |= e4m3_sr(v[4 * w + j], sr_u16(c, 4 * h + j)) << (8 * j);
+                    out[w] = r;
+                }
             }
         }
     }
@@ -136,7 +150,7 @@ __device__ __forceinline__ void encode_block(float (&v)[32], bool pow2, float cv
 // E8M0 path for one block: returns the scale byte; encodes into out.
 template <int ELEM, int RND, int B, int OFF>
 __device__ __forceinline__ uint32_t e8m0_block(float (&v)[32], float amax, bool ceil_rule,
-                                               const uint32_t (&rw)[16], uint32_t (&out)[8]) {
+                                               const SrSource& sr, uint32_t (&out)[8]) {
     int k = (ELEM == ELEM_E2M1) ? e8m0_exp<2, 0x400000u>(amax, ceil_rule)
                                 : e8m0_exp<8, 0x600000u>(amax, ceil_rule);
     const uint32_t sbyte = (uint32_t)(k + 127);
@@ -149,7 +163,7 @@ __device__ __forceinline__ uint32_t e8m0_block(float (&v)[32], float amax, bool 
     const float scale = pow2f(k);
     const float rcp = __builtin_amdgcn_ldexpf(1.0f, -k);
     const float clampv = 448.0f * scale;
-    encode_block<ELEM, RND, B, OFF>(v, true, scale, rcp, clampv, rw, out);
+    encode_block<ELEM, RND, B, OFF>(v, true, scale, rcp, clampv, sr, out);
     return sbyte;
 }
 

@@ -253,7 +253,7 @@ __device__ __forceinline__ float nv_codes_sse(const float (&v)[32], float d, flo
 // candidates are encoded once; the SSE comparison picks one and its codes are kept as they are.
 template <int RND, int OFF>
 __device__ __forceinline__ uint32_t nv_block(float (&v)[32], float amax, float g, bool four_six,
-                                             const uint32_t (&rw)[16], uint32_t (&out)[8]) {
+                                             const SrSource& sr, uint32_t (&out)[8]) {
     float d;
     uint32_t s = nv_candidate(amax, g, 6.0f, d);
     if constexpr (RND == RND_RNE) {
@@ -269,16 +269,16 @@ __device__ __forceinline__ uint32_t nv_block(float (&v)[32], float amax, float g
             return four ? s4 : s;
         }
     }
-    encode_block<ELEM_E2M1, RND, 16, OFF>(v, false, 1.0f, scale_recip(d), 448.0f, rw, out);
+    encode_block<ELEM_E2M1, RND, 16, OFF>(v, false, 1.0f, scale_recip(d), 448.0f, sr, out);
     return s;
 }
 
 // fp32-scale path for one block: writes the scale value.
 template <int ELEM, int RND, int B, int OFF>
-__device__ __forceinline__ float f32_block(float (&v)[32], float amax, const uint32_t (&rw)[16],
+__device__ __forceinline__ float f32_block(float (&v)[32], float amax, const SrSource& sr,
                                            uint32_t (&out)[8]) {
     const float d = amax / (ELEM == ELEM_E2M1 ? 6.0f : 448.0f);
-    encode_block<ELEM, RND, B, OFF>(v, false, 1.0f, scale_recip(d), 448.0f, rw, out);
+    encode_block<ELEM, RND, B, OFF>(v, false, 1.0f, scale_recip(d), 448.0f, sr, out);
     return d;
 }
 
@@ -386,10 +386,7 @@ __global__ __launch_bounds__(kThreads) void k_segment(SegBatch b) {
         return;
     }
     if constexpr (PASS == PASS_QUANT) {
-        uint32_t rw[16];
-        if constexpr (RND == RND_SR) {
-            philox_segment(a.seed, (uint64_t)seg * 32u, rw);
-        }
+        const SrSource sr{a.seed, (uint64_t)seg * 32u};
         uint32_t out[8];
         if constexpr (BR == 32) {
             // tile max over 32 rows: thread (r, j) of the 32 x 8 layout
@@ -399,17 +396,17 @@ __global__ __launch_bounds__(kThreads) void k_segment(SegBatch b) {
             float m = 0.0f;
 #pragma unroll
             for (int r = 0; r < 32; ++r) m = fmaxf(m, tile[r * 8 + (threadIdx.x & 7)]);
-            const uint32_t s = e8m0_block<ELEM, RND, 32, 0>(v, m, a.ceil_rule != 0, rw, out);
+            const uint32_t s = e8m0_block<ELEM, RND, 32, 0>(v, m, a.ceil_rule != 0, sr, out);
             if (valid && (threadIdx.x >> 3) == 0)
                 reinterpret_cast<uint8_t*>(a.scales)[(row >> 5) * spr + sc] = (uint8_t)s;
         } else if constexpr (SC == SC_E8M0) {
             if constexpr (BC == 32) {
-                const uint32_t s = e8m0_block<ELEM, RND, 32, 0>(v, block_amax<32, 0>(v), a.ceil_rule != 0, rw, out);
+                const uint32_t s = e8m0_block<ELEM, RND, 32, 0>(v, block_amax<32, 0>(v), a.ceil_rule != 0, sr, out);
                 if (valid) reinterpret_cast<uint8_t*>(a.scales)[seg] = (uint8_t)s;
             } else {
                 const float m0 = block_amax<16, 0>(v), m1 = block_amax<16, 16>(v);
-                const uint32_t s0 = e8m0_block<ELEM, RND, 16, 0>(v, m0, a.ceil_rule != 0, rw, out);
-                const uint32_t s1 = e8m0_block<ELEM, RND, 16, 16>(v, m1, a.ceil_rule != 0, rw, out);
+                const uint32_t s0 = e8m0_block<ELEM, RND, 16, 0>(v, m0, a.ceil_rule != 0, sr, out);
+                const uint32_t s1 = e8m0_block<ELEM, RND, 16, 16>(v, m1, a.ceil_rule != 0, sr, out);
                 if (valid) reinterpret_cast<uint16_t*>(a.scales)[seg] = (uint16_t)(s0 | (s1 << 8));
             }
         } else if constexpr (SC == SC_NV) {
@@ -422,17 +419,17 @@ __global__ __launch_bounds__(kThreads) void k_segment(SegBatch b) {
                 if (blk == 0 && threadIdx.x == 0) *a.tensor_scale = g;
             }
             const float m0 = block_amax<16, 0>(v), m1 = block_amax<16, 16>(v);
-            const uint32_t s0 = nv_block<RND, 0>(v, m0, g, a.four_six != 0, rw, out);
-            const uint32_t s1 = nv_block<RND, 16>(v, m1, g, a.four_six != 0, rw, out);
+            const uint32_t s0 = nv_block<RND, 0>(v, m0, g, a.four_six != 0, sr, out);
+            const uint32_t s1 = nv_block<RND, 16>(v, m1, g, a.four_six != 0, sr, out);
             if (valid) reinterpret_cast<uint16_t*>(a.scales)[seg] = (uint16_t)(s0 | (s1 << 8));
         } else {  // SC_F32
             if constexpr (BC == 32) {
-                const float d = f32_block<ELEM, RND, 32, 0>(v, block_amax<32, 0>(v), rw, out);
+                const float d = f32_block<ELEM, RND, 32, 0>(v, block_amax<32, 0>(v), sr, out);
                 if (valid) reinterpret_cast<float*>(a.scales)[seg] = d;
             } else {
                 const float m0 = block_amax<16, 0>(v), m1 = block_amax<16, 16>(v);
-                const float d0 = f32_block<ELEM, RND, 16, 0>(v, m0, rw, out);
-                const float d1 = f32_block<ELEM, RND, 16, 16>(v, m1, rw, out);
+                const float d0 = f32_block<ELEM, RND, 16, 0>(v, m0, sr, out);
+                const float d1 = f32_block<ELEM, RND, 16, 16>(v, m1, sr, out);
                 if (valid) reinterpret_cast<float2*>(a.scales)[seg] = make_float2(d0, d1);
             }
         }
