@@ -707,12 +707,24 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
 // ---------------------------------------------------------------------------------------------
 // NVFP4 -> MXFP8 re-expression: one lane per 32-wide K group of one row.
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_nv_to_fp8(const uint8_t* codes, const uint8_t* scales,
-                                                   int64_t rows, int64_t K, uint8_t* out,
-                                                   uint8_t* out_scales) {
-    const int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t groups = rows * (K / 32);
-    if (gi >= groups) return;
+// Both operands in one launch: the first ga groups are A's, the next gb B's.
+struct NvPair {
+    const uint8_t* codes[2];
+    const uint8_t* scales[2];
+    uint8_t* out[2];
+    uint8_t* out_scales[2];
+    int64_t groups[2];
+};
+
+__global__ __launch_bounds__(256) void k_nv_to_fp8(NvPair pr) {
+    int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int op = gi < pr.groups[0] ? 0 : 1;
+    if (op == 1) gi -= pr.groups[0];
+    if (gi >= pr.groups[op]) return;
+    const uint8_t* const codes = op ? pr.codes[1] : pr.codes[0];
+    const uint8_t* const scales = op ? pr.scales[1] : pr.scales[0];
+    uint8_t* const out = op ? pr.out[1] : pr.out[0];
+    uint8_t* const out_scales = op ? pr.out_scales[1] : pr.out_scales[0];
     const u32x4 q = *reinterpret_cast<const u32x4*>(codes + gi * 16);
     const uint32_t s01 = *reinterpret_cast<const uint16_t*>(scales + gi * 2);
     const float s0 = e4m3_value(s01 & 0x7Fu), s1 = e4m3_value((s01 >> 8) & 0x7Fu);
@@ -777,11 +789,9 @@ static hipError_t launch_kind(const GemmArgs& g, int kind, int c_dtype, hipStrea
     if (kind == 1) return launch_out<true, false, false, FQ>(g, c_dtype, s);
     // NVFP4: re-express both operands, then the FP8 product with the tensor scales
     const int64_t ga = g.M * (g.K / 32), gb = g.N * (g.K / 32);
-    hipLaunchKernelGGL(k_nv_to_fp8, dim3((unsigned)((ga + 255) / 256)), dim3(256), 0, s, g.a, g.sa, g.M, g.K, g.a8, g.sa8);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_nv_to_fp8, dim3((unsigned)((gb + 255) / 256)), dim3(256), 0, s, g.b, g.sb, g.N, g.K, g.b8, g.sb8);
-    e = hipGetLastError();
+    NvPair pr{{g.a, g.b}, {g.sa, g.sb}, {g.a8, g.b8}, {g.sa8, g.sb8}, {ga, gb}};
+    hipLaunchKernelGGL(k_nv_to_fp8, dim3((unsigned)((ga + gb + 255) / 256)), dim3(256), 0, s, pr);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     GemmArgs h = g;
     h.a = g.a8;
