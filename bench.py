@@ -54,21 +54,21 @@ HEADLINE = "llama7b_forward_linear"
 WORKLOADS = {
     "llama7b_forward_linear": dict(
         M=4096, N=11008, K=4096, a=dict(hadamard_n=128), b=dict(hadamard_n=128), batched=True,
-        quant="E2M1 + E8M0 per 32 (floor), RNE", fp8=False, f=0.25,
+        quant="E2M1 + E8M0 per 32 (floor), RNE", fp8=False, f=0.375,
         kernel="k_gemm_big (MXFP4, 256x256 tiles, 32x32x64 scaled MFMA, bf16 out)"),
     "backward_2d": dict(
         M=8192, N=4096, K=4096, a=dict(hadamard_n=128, scale="ceil", sr=True),
         b=dict(hadamard_n=128, block=(32, 32), scale="ceil"), batched=False,
         quant="dY: E2M1 + E8M0 per 32 (ceil), Philox SR; W: E2M1 + E8M0 per 32x32 (ceil), RNE",
-        fp8=False, f=0.25, kernel="k_gemm_big (MXFP4, 2D B scales, 256x256 tiles, bf16 out)"),
+        fp8=False, f=0.375, kernel="k_gemm_big (MXFP4, 2D B scales, 256x256 tiles, bf16 out)"),
     "backward_2d_mxfp8": dict(
         M=8192, N=4096, K=4096, a=dict(hadamard_n=128, scale="ceil", sr=True, e4m3=True),
         b=dict(hadamard_n=128, scale="ceil", e4m3=True), batched=False,
         quant="dY: E4M3 + E8M0 per 32 (ceil), Philox SR; W: E4M3 + E8M0 per 32 (ceil), RNE",
-        fp8=True, f=0.25, kernel="k_gemm_big (MXFP8, 256x256 tiles, 32x32x64 scaled MFMA, bf16 out)"),
+        fp8=True, f=0.375, kernel="k_gemm_big (MXFP8, 256x256 tiles, 32x32x64 scaled MFMA, bf16 out)"),
     "nvfp4_4over6": dict(
         M=8192, N=8192, K=8192, a=dict(nv46=True), b=dict(nv46=True), batched=False,
-        quant="E2M1 + E4M3 per 16 x fp32 tensor scale, 4/6 choice, RNE", fp8=True, f=0.125,
+        quant="E2M1 + E4M3 per 16 x fp32 tensor scale, 4/6 choice, RNE", fp8=True, f=0.1875,
         kernel="fp4_gemm call: two NVFP4->FP8 re-expression passes + k_gemm_big (FP8, bf16 out)"),
 }
 
