@@ -12,6 +12,14 @@ forward linear:
   backward_2d_mxfp8  the same with E4M3 elements (MXFP8, the FP8 matrix cores)
   nvfp4_4over6       8192^3: X Laplace with 0.1% x30 outliers, W N(0, 0.02^2), NVFP4 with the
                      4/6 choice (tensor amax pass + quantize), GEMM through the FP8 re-expression
+and three that measure extensions of the path:
+  nvfp4_4over6_given the same with delayed tensor scales (g given, from each tensor's own amax
+                     taken once before timing): one quantize pass per tensor, no amax pass
+  llama7b_fused_out_q the headline with the fused output quantize: C (bf16) and C_q (MXFP4,
+                     H_128 along N, E8M0 floor, RNE) from the GEMM's epilogue
+  backward_dw_colwise dW = dY^T X over 8192 tokens (4096 x 4096 x 8192): dY and X as stored
+                     [tokens, features], quantized column-wise (along tokens, H_128, E8M0 ceil;
+                     dY with Philox SR) without forming the transposes
 Inputs are resident in HBM before timing starts; the step cycles over several copies of the inputs
 (more than the 256 MB last-level cache) so that every step reads its inputs from HBM. Before the
 warm-up steps the step runs untimed for --settle seconds (0.3 s), the time the GPU takes to reach
@@ -69,7 +77,21 @@ WORKLOADS = {
     "nvfp4_4over6": dict(
         M=8192, N=8192, K=8192, a=dict(nv46=True), b=dict(nv46=True), batched=False,
         quant="E2M1 + E4M3 per 16 x fp32 tensor scale, 4/6 choice, RNE", fp8=True, f=0.1875,
-        kernel="fp4_gemm call: two NVFP4->FP8 re-expression passes + k_gemm_big (FP8, bf16 out)"),
+        kernel="fp4_gemm call: NVFP4->FP8 re-expression of both operands + k_gemm_big (FP8, bf16 out)"),
+    "nvfp4_4over6_given": dict(
+        M=8192, N=8192, K=8192, a=dict(nv46=True, given=True), b=dict(nv46=True, given=True), batched=False,
+        quant="E2M1 + E4M3 per 16 x given fp32 tensor scale, 4/6 choice, RNE", fp8=True, f=0.1875,
+        kernel="fp4_gemm call: NVFP4->FP8 re-expression of both operands + k_gemm_big (FP8, bf16 out)"),
+    "llama7b_fused_out_q": dict(
+        M=4096, N=11008, K=4096, a=dict(hadamard_n=128), b=dict(hadamard_n=128), batched=True,
+        out_q=dict(hadamard_n=128),
+        quant="E2M1 + E8M0 per 32 (floor), RNE; C_q: the same along N after H_128", fp8=False, f=0.375,
+        kernel="k_gemm_big (MXFP4, bf16 C + fused H_128 MXFP4 quantize of C along N)"),
+    "backward_dw_colwise": dict(
+        M=4096, N=4096, K=8192, a=dict(hadamard_n=128, scale="ceil", sr=True),
+        b=dict(hadamard_n=128, scale="ceil"), batched=False, colwise=True,
+        quant="column-wise (along tokens): dY E2M1 + E8M0 per 32 (ceil), Philox SR; X the same, RNE",
+        fp8=False, f=0.375, kernel="k_gemm_big (MXFP4, 256x256 tiles, bf16 out)"),
 }
 
 
@@ -93,7 +115,8 @@ def parse():
 def params_of(fp4, spec):
     """fp4.Params for one operand's quantization spec."""
     if spec.get("nv46"):
-        return fp4.Params(block=(1, 16), scale_mode=fp4.SCALE_NV_4OVER6)
+        return fp4.Params(block=(1, 16),
+                          scale_mode=fp4.SCALE_NV_4OVER6_GIVEN if spec.get("given") else fp4.SCALE_NV_4OVER6)
     return fp4.Params(elem=fp4.E4M3 if spec.get("e4m3") else fp4.E2M1, block=spec.get("block", (1, 32)),
                       scale_mode=fp4.SCALE_E8M0_CEIL if spec.get("scale") == "ceil" else fp4.SCALE_E8M0_FLOOR,
                       round_mode=fp4.ROUND_SR if spec.get("sr") else fp4.ROUND_RNE,
@@ -109,7 +132,24 @@ def inputs_of(name):
     if name.startswith("backward_2d"):
         w, dy = wl.backward_2d(0)
         return dy, w
+    if name == "llama7b_fused_out_q":
+        x, w, _ = wl.llama_linear(0)
+        return x, w
+    if name == "backward_dw_colwise":
+        return wl.backward_dw(0)  # dY [tokens, 4096], X [tokens, 4096]
     return wl.nvfp4_4over6(0)
+
+
+def given_scale(bits) -> float:
+    """The delayed tensor scale of a bf16 tensor taken from its own amax: RN(amax / 2688) in fp32
+    (1 for an all-zero tensor)."""
+    amax = np.float32(np.abs(workloads_f32(bits)).max())
+    return float(amax / np.float32(2688.0)) if amax > 0 else 1.0
+
+
+def workloads_f32(bits):
+    from bit_gemm_fwht_amd import workloads as wl
+    return wl.bf16_bits_to_f32(bits)
 
 
 def measured_traffic():
@@ -193,22 +233,30 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
-def cpu_baseline(wk, a_bits, b_bits, pa, pb, f):
-    """Time the oracle on f*M rows of A, f*N rows of B and the f*M x f*N block of C, and scale to
-    a whole step: T = T_quantize / f + T_gemm / f^2."""
+def cpu_baseline(wk, a_bits, b_bits, pa, pb, f, out_q=None, ga=None, gb=None):
+    """Time the oracle on f*M rows of A, f*N rows of B and the f*M x f*N block of C (and its output
+    quantize), and scale to a whole step: T = T_quantize / f + T_gemm / f^2. Column-wise operands
+    sample columns of the stored tensors (rows of their transposes)."""
     import oracle as orc
     M, N, K = wk["M"], wk["N"], wk["K"]
     sm, sn = max(int(M * f) // 32 * 32, 32), max(int(N * f) // 32 * 32, 32)  # whole 32-row tiles
-    As = np.ascontiguousarray(a_bits[:sm])
-    Bs = np.ascontiguousarray(b_bits[:sn])
+    if out_q is not None and out_q.hadamard_n:  # C's sampled rows hold whole rotation chunks
+        sn = max(sn // out_q.hadamard_n * out_q.hadamard_n, out_q.hadamard_n)
+    if wk.get("colwise"):
+        As = np.ascontiguousarray(a_bits[:, :sm].T)
+        Bs = np.ascontiguousarray(b_bits[:, :sn].T)
+    else:
+        As = np.ascontiguousarray(a_bits[:sm])
+        Bs = np.ascontiguousarray(b_bits[:sn])
 
-    def q(x, p):
+    def q(x, p, ts=None):
         return orc.quantize(x, elem=p.elem, block=p.block, scale_mode=p.scale_mode,
-                            round_mode=p.round_mode, hadamard_n=p.hadamard_n, seed=p.seed)
+                            round_mode=p.round_mode, hadamard_n=p.hadamard_n, seed=p.seed,
+                            tensor_scale=ts)
 
     t0 = time.perf_counter()
-    ca, sa, ta = q(As, pa)
-    cb, sb, tb = q(Bs, pb)
+    ca, sa, ta = q(As, pa, ga)
+    cb, sb, tb = q(Bs, pb, gb)
     t1 = time.perf_counter()
     a64 = orc.operand_f64(ca, sa, ta, sm, K, elem=pa.elem, block=pa.block, scale_mode=pa.scale_mode)
     if pb.block[0] == 1:
@@ -216,7 +264,9 @@ def cpu_baseline(wk, a_bits, b_bits, pa, pb, f):
     else:  # 2D tiles: each row takes its tile row's scales
         srow = np.ascontiguousarray(sb.reshape(sn // 32, -1)[np.arange(sn) // 32])
         b64 = orc.operand_f64(cb, srow, tb, sn, K, elem=pb.elem, block=(1, 32), scale_mode=pb.scale_mode)
-    orc.gemm_f64(a64, b64)
+    c64, _ = orc.gemm_f64(a64, b64)
+    if out_q is not None:
+        q(c64.astype(np.float32), out_q)
     t2 = time.perf_counter()
     fm, fn = sm / M, sn / N
     t_step = (t1 - t0) / ((fm + fn) / 2) + (t2 - t1) / (fm * fn)
@@ -226,8 +276,9 @@ def cpu_baseline(wk, a_bits, b_bits, pa, pb, f):
         "cores": 1,
         "kind": "oracle",
         "sample": (f"oracle quantize of {sm} A rows + {sn} B rows ({t1 - t0:.2f} s) and the fp64 "
-                   f"GEMM of their {sm}x{sn} block over K={K} ({t2 - t1:.2f} s), scaled to a full "
-                   f"step as T_q/f + T_gemm/f^2 with f={f} (the sampled row fractions)"),
+                   f"GEMM of their {sm}x{sn} block over K={K}"
+                   f"{' with its output quantize' if out_q is not None else ''} ({t2 - t1:.2f} s), "
+                   f"scaled to a full step as T_q/f + T_gemm/f^2 with f={f} (the sampled row fractions)"),
         "step_s": round(t_step, 3),
     }
 
@@ -258,6 +309,20 @@ def main():
     qa = [fp4.empty_qtensor(M, K, pa, dev) for _ in range(args.copies)]
     qb = [fp4.empty_qtensor(N, K, pb, dev) for _ in range(args.copies)]
     cs = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(args.copies)]
+    colwise = bool(wk.get("colwise"))
+    quantize_one = fp4.quantize_colwise if colwise else fp4.quantize
+    # delayed tensor scales: g of each tensor from its own amax, set once in the outputs' buffers
+    ga = gb = None
+    if wk["a"].get("given"):
+        ga, gb = given_scale(a_bits), given_scale(b_bits)
+        for q in qa:
+            q.tensor_scale.fill_(ga)
+        for q in qb:
+            q.tensor_scale.fill_(gb)
+    oq = cq = None
+    if wk.get("out_q"):
+        oq = fp4.Params(hadamard_n=wk["out_q"]["hadamard_n"])
+        cq = [fp4.empty_qtensor(M, N, oq, dev) for _ in range(args.copies)]
     # workspaces allocated once, outside the timed region
     wsa = wsb = wsg = None
     nb = fp4.buffer_sizes(M, K, pa)[2]
@@ -280,11 +345,16 @@ def main():
         if wk["batched"]:
             fp4.quantize_batch([As[j], Bs[j]], pa, outs=[qa[j], qb[j]])
         else:
-            fp4.quantize(As[j], pa, out=qa[j], workspace=wsa)
-            fp4.quantize(Bs[j], pb, out=qb[j], workspace=wsb)
+            quantize_one(As[j], pa, out=qa[j], workspace=wsa,
+                         tensor_scale=qa[j].tensor_scale if ga is not None else None)
+            quantize_one(Bs[j], pb, out=qb[j], workspace=wsb,
+                         tensor_scale=qb[j].tensor_scale if gb is not None else None)
         if ev is not None:
             ev[2 * i + 1].record()
-        fp4.gemm(qa[j], qb[j], out=cs[j], workspace=wsg)
+        if oq is not None:
+            fp4.gemm(qa[j], qb[j], out=cs[j], workspace=wsg, out_q=oq, q_out=cq[j])
+        else:
+            fp4.gemm(qa[j], qb[j], out=cs[j], workspace=wsg)
 
     # The GPU's clocks ramp up over the first tens of milliseconds of sustained work (a step runs
     # ~15 % slower at first): run the step untimed for --settle seconds before the warm-up steps,
@@ -321,7 +391,7 @@ def main():
     bytes_q = qbytes(M, pa) + qbytes(N, pb)
     gemm_tflops = flops / t_g / 1e12
     peak = FP8_PEAK_TFLOPS if wk["fp8"] else FP4_PEAK_TFLOPS
-    dtype = {False: "mxfp4", True: "mxfp8"}[wk["fp8"]] if args.workload != "nvfp4_4over6" else "nvfp4"
+    dtype = "nvfp4" if args.workload.startswith("nvfp4") else {False: "mxfp4", True: "mxfp8"}[wk["fp8"]]
     out = {
         "metric": "quantize GB/s (% HBM peak); MXFP4 GEMM TFLOP/s (% FP4 MFMA peak)",
         "value": round(flops / (wall / args.steps) / 1e12, 3),
@@ -346,13 +416,17 @@ def main():
                      "frac": round(bytes_q / tq / 1e9 / HBM_PEAK_GBS, 4),
                      "us": round(tq * 1e6, 2), "bytes": int(bytes_q),
                      "launches": ("one batched k_segment launch for A and B" if wk["batched"]
-                                  else "separate launches for A and B")},
+                                  else "separate launches for A and B")
+                     + (", column-wise" if colwise else "") + (", given tensor scales" if ga is not None else "")},
         "gemm": {"TFLOP/s": round(gemm_tflops, 2), "frac": round(gemm_tflops / peak, 4),
                  "us": round(t_g * 1e6, 2), "flops": flops},
     }
+    if oq is not None:
+        cb, sb, _ = fp4.buffer_sizes(M, N, oq)
+        out["gemm"]["fused_out_q"] = f"C (bf16) and C_q ({cb + sb} bytes: MXFP4 along N after H_{oq.hadamard_n})"
     if not args.no_cpu_baseline:
         f = args.cpu_fraction if args.cpu_fraction is not None else wk["f"]
-        out["cpu_baseline"] = cpu_baseline(wk, a_bits, b_bits, pa, pb, f)
+        out["cpu_baseline"] = cpu_baseline(wk, a_bits, b_bits, pa, pb, f, out_q=oq, ga=ga, gb=gb)
     print(json.dumps(out), flush=True)
 
 

@@ -172,7 +172,8 @@ def _set_given_scale(q: QTensor, params: Params, tensor_scale) -> None:
         if tensor_scale is None:
             raise ValueError("the _GIVEN scale modes need tensor_scale (the fp32 g)")
         if isinstance(tensor_scale, torch.Tensor):
-            q.tensor_scale.copy_(tensor_scale.reshape(1))
+            if tensor_scale.data_ptr() != q.tensor_scale.data_ptr():  # else g is in place already
+                q.tensor_scale.copy_(tensor_scale.reshape(1))
         else:
             q.tensor_scale.fill_(float(tensor_scale))
 

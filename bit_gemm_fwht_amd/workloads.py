@@ -15,6 +15,8 @@ used trained weights or datasets that are not available here):
   backward_2d   W bf16 4096x4096 ~ N(0, 0.02^2); dY bf16 8192x4096 ~ Student-t(3) x 1e-3.
   nvfp4_4over6  X bf16 8192x8192 ~ Laplace(0,1) with 0.1% of entries x30; W bf16 8192x8192
                 ~ N(0, 0.02^2).
+  backward_dw   dY bf16 8192x4096 ~ Student-t(3) x 1e-3 and X bf16 8192x4096 ~ N(0,1) with 1% of
+                channels x20: the operands of dW = dY^T X (the column-wise quantize).
 Every generator takes its own numpy Generator seeded with `seed`, and draws the tensors in the
 order listed. bf16 tensors are returned as uint16 bit patterns (round-to-nearest-even of the fp32
 draw).
@@ -91,6 +93,18 @@ def nvfp4_4over6(seed: int = 0, m: int = 8192, n: int = 8192, k: int = 8192):
     x.reshape(-1)[idx] *= np.float32(30.0)
     w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
     return f32_to_bf16_bits(x), f32_to_bf16_bits(w)
+
+
+def backward_dw(seed: int = 0, t: int = 8192, d_out: int = 4096, d_in: int = 4096):
+    """dY [t, d_out] ~ Student-t(3) * 1e-3 and X [t, d_in] ~ N(0, 1) with 1% of channels x20, as
+    bf16 bits: the two operands of the weight gradient dW = dY^T X, which contracts over the token
+    axis t (the first axis of both as stored)."""
+    rng = np.random.default_rng(seed)
+    dy = (rng.standard_t(3.0, size=(t, d_out)) * 1e-3).astype(np.float32)
+    x = rng.standard_normal((t, d_in), dtype=np.float32)
+    ch = rng.choice(d_in, size=int(round(0.01 * d_in)), replace=False)
+    x[:, ch] *= np.float32(20.0)
+    return f32_to_bf16_bits(dy), f32_to_bf16_bits(x)
 
 
 def scaled_down(kind: str, seed: int = 0, **shape):

@@ -44,7 +44,7 @@ def test_workload_quantization_is_valid(fp4, name):
         per = 1 if p.elem == fp4.E4M3 else 0.5
         assert codes == int(rows * wk["K"] * per)
         assert scales > 0
-    assert wk["fp8"] == (bench.params_of(fp4, wk["a"]).elem == fp4.E4M3 or name == "nvfp4_4over6")
+    assert wk["fp8"] == (bench.params_of(fp4, wk["a"]).elem == fp4.E4M3 or name.startswith("nvfp4"))
 
 
 def test_traffic_summary_is_read_only_for_the_current_kernel(tmp_path, monkeypatch):
@@ -96,3 +96,27 @@ def test_nvfp4_4over6_recipe():
     # with probability e^-30, a scaled one with probability e^-1, so about 1049 / e = 386 do
     assert 300 < np.sum(xf > 30.0) < 480
     assert abs(np.median(xf) - np.log(2.0)) < 0.02
+
+
+def test_backward_dw_recipe():
+    dy, x = wl.backward_dw(0, t=1024, d_out=256, d_in=512)
+    assert dy.shape == (1024, 256) and x.shape == (1024, 512)
+    d = wl.bf16_bits_to_f32(dy).astype(np.float64) / 1e-3
+    assert abs(np.median(np.abs(d)) - 0.765) < 0.03  # Student-t(3)
+    xf = wl.bf16_bits_to_f32(x)
+    s = xf.std(axis=0)
+    assert np.sum(s > 10) == 5  # 1 % of 512 channels (rounded) scaled x20
+
+
+def test_given_scale_is_the_tensors_own_nvfp4_scale():
+    """The delayed tensor scale the benchmark hands the _GIVEN modes is RN(amax / 2688), the scale
+    the plain NVFP4 mode computes, so both modes give the same codes."""
+    import oracle as orc
+    rng = np.random.default_rng(3)
+    x = wl.f32_to_bf16_bits(rng.laplace(size=(64, 256)).astype(np.float32))
+    g = bench.given_scale(x)
+    _, _, ts = orc.quantize(x, block=(1, 16), scale_mode=orc.SCALE_NV_4OVER6)
+    assert np.float32(g) == ts.reshape(-1)[0]
+    c1, s1, _ = orc.quantize(x, block=(1, 16), scale_mode=orc.SCALE_NV_4OVER6)
+    c2, s2, _ = orc.quantize(x, block=(1, 16), scale_mode=orc.SCALE_NV_4OVER6_GIVEN, tensor_scale=g)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)

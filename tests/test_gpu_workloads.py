@@ -88,3 +88,55 @@ def test_nvfp4_4over6(orc):
     qx, ox = _quant_both(orc, x, p)
     qw, ow = _quant_both(orc, w, p)
     _sampled_gemm(orc, qx, qw, ox, ow, p, p, torch.bfloat16)
+
+
+def test_nvfp4_4over6_given_scale(orc):
+    """The delayed-scale workload: with g handed in as each tensor's own RN(amax / 2688), the
+    _GIVEN mode's codes and scales equal the oracle's plain NVFP4 + 4/6 quantization (one pass)."""
+    x, _ = wl.nvfp4_4over6(0)
+    amax = np.float32(np.abs(wl.bf16_bits_to_f32(x)).max())
+    g = float(amax / np.float32(2688.0))
+    q = fp4.quantize(_to_dev(x), P(block=(1, 16), scale_mode=fp4.SCALE_NV_4OVER6_GIVEN), tensor_scale=g)
+    torch.cuda.synchronize()
+    oc, os_, ots = _orc_quant(orc, x, P(block=(1, 16), scale_mode=NV46))
+    assert np.array_equal(q.codes.cpu().numpy(), oc.reshape(-1)), "codes differ from the oracle"
+    assert np.array_equal(q.scales.cpu().numpy(), os_.reshape(-1).view(np.uint8)), "scales differ"
+    assert q.tensor_scale.cpu().numpy().view(np.uint32)[0] == ots.view(np.uint32)[0]
+
+
+def test_llama7b_fused_output_quantize(orc):
+    """The headline GEMM with the fused H_128 MXFP4 output quantize: sampled rows of C_q equal the
+    oracle's quantization of the same rows of the fp32 C the call stores."""
+    x, w, _ = wl.llama_linear(0)
+    p = P(hadamard_n=128)
+    qx, qw = fp4.quantize_batch([_to_dev(x), _to_dev(w)], p)
+    oq = P(hadamard_n=128)
+    c, cq = fp4.gemm(qx, qw, out_dtype=torch.float32, out_q=oq)
+    torch.cuda.synchronize()
+    M, N = c.shape
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(5).integers(0, M, 62)]))
+    c_rows = c[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    oc, os_, _ = _orc_quant(orc, c_rows, oq)
+    codes = cq.codes.view(M, N // 2)[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    scales = cq.scales.view(M, N // 32)[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    assert np.array_equal(codes, oc.reshape(len(rows), N // 2)), "C_q codes differ from the oracle"
+    assert np.array_equal(scales, os_.reshape(len(rows), N // 32).view(np.uint8)), "C_q scales differ"
+
+
+def test_backward_dw_colwise(orc):
+    """dW = dY^T X over 8192 tokens: dY and X (as stored, [tokens, 4096]) quantized column-wise
+    (H_128 along tokens, E8M0 ceil; dY SR) equal the oracle's quantization of the transposes; the
+    4096x4096x8192 GEMM on sampled outputs."""
+    dy, x = wl.backward_dw(0)
+    pd = P(scale_mode=CEIL, round_mode=SR, hadamard_n=128, seed=7)
+    px = P(scale_mode=CEIL, hadamard_n=128)
+    qs, os_ = [], []
+    for t, p in ((dy, pd), (x, px)):
+        q = fp4.quantize_colwise(_to_dev(t), p)
+        torch.cuda.synchronize()
+        o = _orc_quant(orc, np.ascontiguousarray(t.T), p)
+        assert np.array_equal(q.codes.cpu().numpy(), o[0].reshape(-1)), "codes differ from the oracle"
+        assert np.array_equal(q.scales.cpu().numpy(), o[1].reshape(-1).view(np.uint8)), "scales differ"
+        qs.append(q)
+        os_.append(o)
+    _sampled_gemm(orc, qs[0], qs[1], os_[0], os_[1], pd, px, torch.bfloat16)
