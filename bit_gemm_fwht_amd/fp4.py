@@ -292,8 +292,14 @@ def gemm(a: QTensor, b: QTensor, out_dtype=torch.bfloat16, out: torch.Tensor | N
 
     With out_q (MX groups of 32 along N, E8M0 floor / ceil, RNE or SR, optionally rotated along N
     with out_q.hadamard_n <= 128), C is also quantized in the epilogue and (C, C_q) is returned;
-    keep_c=False skips writing C and returns (None, C_q)."""
+    keep_c=False skips writing C and returns (None, C_q). out may be a column block of a wider
+    row-major buffer (its row pitch is passed as ldc)."""
     dev = a.codes.device
+    if out is not None:
+        if out.dim() != 2 or tuple(out.shape) != (a.rows, b.rows) or out.device != dev:
+            raise ValueError(f"out must be a [{a.rows}, {b.rows}] tensor on {dev}")
+        if out.stride(1) != 1 or out.stride(0) < b.rows:
+            raise ValueError("out must be row-major: unit column stride, row pitch >= N")
     c = None
     if out_q is None or keep_c:
         c = out if out is not None else torch.empty(a.rows, b.rows, dtype=out_dtype, device=dev)

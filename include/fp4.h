@@ -186,7 +186,9 @@ int fp4_hadamard(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int
                  int32_t hadamard_n, float* y, void* stream);
 
 /* C [M, N] = A [M, K] * B [N, K]^T on the quantized operands, fp32 accumulation; C fp32 or bf16
- * (round to nearest even) with leading dimension ldc >= N. Supported operand pairs:
+ * (round to nearest even) with leading dimension ldc >= N (elements; C itself 16-byte aligned, else
+ * FP4_ERR_ALIGNMENT; a pitch that is not a multiple of 16 bytes only narrows the stores), so C may
+ * be a column block of a wider row-major buffer. Supported operand pairs:
  * MXFP4 x MXFP4 (E2M1, E8M0 (1, 32) groups; B may use (32, 32) 2D tiles), MXFP8 x MXFP8 (E4M3,
  * E8M0 (1, 32)), and NVFP4 x NVFP4 (E2M1, (1, 16) NV or 4/6 scales: each 32-wide K group is
  * re-expressed as E4M3 elements under one power-of-two scale and multiplied on the FP8 matrix

@@ -239,3 +239,18 @@ def test_nv_given_validation_without_device(fp4):
     assert _quant(fp4, P(fp4, scale_mode=6, block_cols=32), ts=0x4000) == E.ERR_UNSUPPORTED
     assert _quant(fp4, P(fp4, scale_mode=6, block_cols=16, round_mode=1), ts=0x4000) == E.ERR_UNSUPPORTED
     assert _quant(fp4, P(fp4, scale_mode=7, block_cols=16), ts=0x4000) == E.ERR_INVALID_ARG
+
+
+def test_binding_refuses_an_output_that_is_not_row_major(fp4):
+    """The binding passes out.stride(0) as ldc, so it accepts any row pitch >= N but refuses an out
+    whose columns are not contiguous, or of the wrong shape (checked before anything is launched)."""
+    import torch
+    p = fp4.Params()
+    a = fp4.QTensor(torch.zeros(64 * 128, dtype=torch.uint8), torch.zeros(64 * 8, dtype=torch.uint8),
+                    None, 64, 256, p)
+    b = fp4.QTensor(torch.zeros(96 * 128, dtype=torch.uint8), torch.zeros(96 * 8, dtype=torch.uint8),
+                    None, 96, 256, p)
+    with pytest.raises(ValueError, match="row-major"):
+        fp4.gemm(a, b, out=torch.empty(96, 64, dtype=torch.bfloat16).t())
+    with pytest.raises(ValueError):
+        fp4.gemm(a, b, out=torch.empty(64, 95, dtype=torch.bfloat16))

@@ -573,3 +573,35 @@ def test_nvfp4_given_tensor_scale_parity(orc, mode, gfac, hn, rnd):
         tol = _gemm_tol(ref.reshape(-1), sabs.reshape(-1), a64, b64, im, inn, params, 256,
                         torch.float32).reshape(256, 160)
         assert np.all(np.abs(c.cpu().numpy() - ref) <= tol)
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 768, 1024), (300, 544, 640), (200, 160, 384)])
+@pytest.mark.parametrize("kind", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("c_dtype", [torch.bfloat16, torch.float32])
+def test_gemm_into_a_column_block(M, N, K, kind, c_dtype):
+    """C written into a column block of a wider buffer (row pitch ldc > N; block start 16-byte
+    aligned, pitch a multiple of 16 bytes or not): the block holds exactly the contiguous call's C
+    (itself checked against the oracle above) and no element outside it changes; a block start
+    that is not 16-byte aligned is refused."""
+    rng = np.random.default_rng(M + 3 * N + K)
+    a = torch.from_numpy(wl.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32)).view(np.int16))
+    b = torch.from_numpy(wl.f32_to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32)).view(np.int16))
+    a, b = a.to(DEV).view(torch.bfloat16), b.to(DEV).view(torch.bfloat16)
+    if kind == "mxfp4":
+        pa, pb = P(hadamard_n=128), P(hadamard_n=128, scale_mode=CEIL)
+    else:
+        pa, pb = P(block=(1, 16), scale_mode=NV46), P(block=(1, 16), scale_mode=NV)
+    qa, qb = fp4.quantize(a, pa), fp4.quantize(b, pb)
+    ref = fp4.gemm(qa, qb, out_dtype=c_dtype)
+    ibits = torch.int16 if c_dtype == torch.bfloat16 else torch.int32
+    for col0, pad in ((0, 64), (16, 48), (0, 3), (16, 1)):
+        wide = torch.full((M, col0 + N + pad), -7.25, dtype=c_dtype, device=DEV)
+        got = fp4.gemm(qa, qb, out=wide[:, col0:col0 + N])
+        torch.cuda.synchronize()
+        assert got.data_ptr() == wide[:, col0:].data_ptr()
+        assert torch.equal(wide[:, col0:col0 + N].contiguous().view(ibits), ref.view(ibits)), (col0, pad)
+        outside = torch.cat([wide[:, :col0].reshape(-1), wide[:, col0 + N:].reshape(-1)])
+        assert bool((outside == -7.25).all()), f"elements outside the block changed ({col0}, {pad})"
+    wide = torch.zeros((M, N + 8), dtype=c_dtype, device=DEV)
+    with pytest.raises(fp4.Fp4Error):
+        fp4.gemm(qa, qb, out=wide[:, 1:N + 1])
