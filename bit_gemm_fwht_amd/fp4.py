@@ -178,6 +178,36 @@ def _set_given_scale(q: QTensor, params: Params, tensor_scale) -> None:
             q.tensor_scale.fill_(float(tensor_scale))
 
 
+def _on(dev, *ts) -> None:
+    """Every buffer handed to the library must be device memory of the device the call runs on."""
+    for t in ts:
+        if t is not None and (not t.is_cuda or t.device != dev):
+            raise ValueError(f"a buffer on {t.device} was passed to a call that runs on {dev}")
+
+
+def _check_q(q: QTensor, rows: int, cols: int, params: Params, dev, what: str) -> None:
+    """q's buffers hold at least what a rows x cols tensor quantized with params takes."""
+    cb, sb, _ = buffer_sizes(rows, cols, params)
+    for t, need, name in ((q.codes, cb, "codes"), (q.scales, sb, "scales")):
+        if not t.is_contiguous() or t.numel() * t.element_size() < need:
+            raise ValueError(f"{what}.{name} must be contiguous and hold at least {need} bytes")
+        _on(dev, t)
+    if params.scale_mode in NV_MODES:
+        if q.tensor_scale is None or q.tensor_scale.dtype != torch.float32 or q.tensor_scale.numel() < 1:
+            raise ValueError(f"{what} needs a one-element float32 tensor_scale buffer")
+        _on(dev, q.tensor_scale)
+
+
+def _ws_bytes(ws: torch.Tensor | None, need: int, dev) -> int:
+    if ws is None:
+        return 0
+    _on(dev, ws)
+    nb = ws.numel() * ws.element_size()
+    if not ws.is_contiguous() or nb < need:
+        raise ValueError(f"workspace must be contiguous and hold at least {need} bytes")
+    return nb
+
+
 def quantize(x: torch.Tensor, params: Params = MXFP4, out: QTensor | None = None,
              workspace: torch.Tensor | None = None, tensor_scale=None) -> QTensor:
     """Quantize a 2-D float32 / bfloat16 CUDA tensor along its last axis. tensor_scale: g for the
@@ -187,17 +217,19 @@ def quantize(x: torch.Tensor, params: Params = MXFP4, out: QTensor | None = None
     if x.stride(1) != 1:
         raise ValueError("x must be contiguous along its last axis")
     rows, cols = x.shape
+    if out is not None:
+        _check_q(out, rows, cols, params, x.device, "out")
     q = out if out is not None else empty_qtensor(rows, cols, params, x.device)
     _set_given_scale(q, params, tensor_scale)
     _, _, wb = buffer_sizes(rows, cols, params)
     if wb and workspace is None:
         workspace = torch.empty(wb, dtype=torch.uint8, device=x.device)
+    wsb = _ws_bytes(workspace, wb, x.device)
     p = params.c()
     ts = q.tensor_scale.data_ptr() if q.tensor_scale is not None else None
     st = lib().fp4_quantize(x.data_ptr(), _dtype_code(x), rows, cols, x.stride(0), ctypes.byref(p),
                             q.codes.data_ptr(), q.scales.data_ptr(), ts,
-                            workspace.data_ptr() if workspace is not None else None,
-                            workspace.numel() if workspace is not None else 0,
+                            workspace.data_ptr() if workspace is not None else None, wsb,
                             _stream_ptr(x.device))
     _check(st, "fp4_quantize")
     return q
@@ -219,7 +251,10 @@ def quantize_batch(xs, params: Params = MXFP4, outs=None, tensor_scales=None) ->
             raise ValueError("each x must be a 2-D CUDA tensor, contiguous along its last axis")
         if x.dtype != xs[0].dtype:
             raise ValueError("all tensors of a batch share one dtype")
+        _on(xs[0].device, x)
         rows, cols = x.shape
+        if outs[i] is not None:
+            _check_q(outs[i], rows, cols, params, x.device, f"outs[{i}]")
         q = outs[i] if outs[i] is not None else empty_qtensor(rows, cols, params, x.device)
         _set_given_scale(q, params, tss[i])
         ts = q.tensor_scale.data_ptr() if q.tensor_scale is not None else None
@@ -240,24 +275,33 @@ def quantize_colwise(x: torch.Tensor, params: Params = MXFP4, out: QTensor | Non
     if x.stride(1) != 1:
         raise ValueError("x must be contiguous along its last axis")
     rows, cols = x.shape
+    if out is not None:
+        _check_q(out, cols, rows, params, x.device, "out")
     q = out if out is not None else empty_qtensor(cols, rows, params, x.device)
     _set_given_scale(q, params, tensor_scale)
     _, _, wb = buffer_sizes(cols, rows, params)
     if wb and workspace is None:
         workspace = torch.empty(wb, dtype=torch.uint8, device=x.device)
+    wsb = _ws_bytes(workspace, wb, x.device)
     p = params.c()
     ts = q.tensor_scale.data_ptr() if q.tensor_scale is not None else None
     st = lib().fp4_quantize_colwise(x.data_ptr(), _dtype_code(x), rows, cols, x.stride(0),
                                     ctypes.byref(p), q.codes.data_ptr(), q.scales.data_ptr(), ts,
-                                    workspace.data_ptr() if workspace is not None else None,
-                                    workspace.numel() if workspace is not None else 0,
+                                    workspace.data_ptr() if workspace is not None else None, wsb,
                                     _stream_ptr(x.device))
     _check(st, "fp4_quantize_colwise")
     return q
 
 
 def dequantize(q: QTensor, dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
-    y = out if out is not None else torch.empty(q.rows, q.cols, dtype=dtype, device=q.codes.device)
+    """Decode q to float32 / bfloat16 [rows, cols] (out: any row pitch >= cols)."""
+    dev = q.codes.device
+    _check_q(q, q.rows, q.cols, q.params, dev, "q")
+    if out is not None:
+        _on(dev, out)
+        if out.dim() != 2 or tuple(out.shape) != (q.rows, q.cols) or out.stride(1) != 1 or out.stride(0) < q.cols:
+            raise ValueError(f"out must be a row-major [{q.rows}, {q.cols}] tensor")
+    y = out if out is not None else torch.empty(q.rows, q.cols, dtype=dtype, device=dev)
     p = q.params.c()
     ts = q.tensor_scale.data_ptr() if q.tensor_scale is not None else None
     st = lib().fp4_dequantize(q.codes.data_ptr(), q.scales.data_ptr(), ts, q.rows, q.cols,
@@ -268,8 +312,14 @@ def dequantize(q: QTensor, dtype=torch.float32, out: torch.Tensor | None = None)
 
 
 def hadamard(x: torch.Tensor, n: int, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Blockwise H_n / sqrt(n) along the last axis (fp32 result)."""
+    """Blockwise H_n / sqrt(n) along the last axis (fp32 result, contiguous)."""
+    if x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D CUDA tensor, contiguous along its last axis")
     rows, cols = x.shape
+    if out is not None:
+        _on(x.device, out)
+        if out.dtype != torch.float32 or tuple(out.shape) != (rows, cols) or not out.is_contiguous():
+            raise ValueError(f"out must be a contiguous float32 [{rows}, {cols}] tensor")
     y = out if out is not None else torch.empty(rows, cols, dtype=torch.float32, device=x.device)
     st = lib().fp4_hadamard(x.data_ptr(), _dtype_code(x), rows, cols, x.stride(0), n, y.data_ptr(),
                             _stream_ptr(x.device))
@@ -300,6 +350,8 @@ def gemm(a: QTensor, b: QTensor, out_dtype=torch.bfloat16, out: torch.Tensor | N
             raise ValueError(f"out must be a [{a.rows}, {b.rows}] tensor on {dev}")
         if out.stride(1) != 1 or out.stride(0) < b.rows:
             raise ValueError("out must be row-major: unit column stride, row pitch >= N")
+    _check_q(a, a.rows, a.cols, a.params, dev, "a")
+    _check_q(b, b.rows, b.cols, b.params, dev, "b")
     c = None
     if out_q is None or keep_c:
         c = out if out is not None else torch.empty(a.rows, b.rows, dtype=out_dtype, device=dev)
@@ -311,6 +363,8 @@ def gemm(a: QTensor, b: QTensor, out_dtype=torch.bfloat16, out: torch.Tensor | N
     if out_q is not None:
         if q_out is None:
             q_out = empty_qtensor(a.rows, b.rows, out_q, dev)
+        else:
+            _check_q(q_out, a.rows, b.rows, out_q, dev, "q_out")
         qp = out_q.c()
         qc = q_out.c()
     st = lib().fp4_gemm(ctypes.byref(ac), ctypes.byref(bc), c.data_ptr() if c is not None else None,
@@ -318,7 +372,7 @@ def gemm(a: QTensor, b: QTensor, out_dtype=torch.bfloat16, out: torch.Tensor | N
                         ctypes.byref(qp) if qp is not None else None,
                         ctypes.byref(qc) if qc is not None else None,
                         workspace.data_ptr() if workspace is not None else None,
-                        workspace.numel() if workspace is not None else 0, _stream_ptr(dev))
+                        _ws_bytes(workspace, wb, dev), _stream_ptr(dev))
     _check(st, "fp4_gemm")
     if out_q is not None:
         return c, q_out

@@ -254,3 +254,23 @@ def test_binding_refuses_an_output_that_is_not_row_major(fp4):
         fp4.gemm(a, b, out=torch.empty(96, 64, dtype=torch.bfloat16).t())
     with pytest.raises(ValueError):
         fp4.gemm(a, b, out=torch.empty(64, 95, dtype=torch.bfloat16))
+
+
+def test_binding_refuses_host_and_undersized_buffers(fp4):
+    """A host pointer handed to a kernel would fault the GPU: the binding refuses host tensors and
+    operand buffers smaller than the size queries state, before anything is launched."""
+    import torch
+    p = fp4.Params()
+    a = fp4.QTensor(torch.zeros(64 * 128, dtype=torch.uint8), torch.zeros(64 * 8, dtype=torch.uint8),
+                    None, 64, 256, p)
+    with pytest.raises(ValueError, match="buffer on cpu"):
+        fp4.gemm(a, a)
+    with pytest.raises(ValueError, match="buffer on cpu"):
+        fp4.dequantize(a)
+    with pytest.raises(ValueError, match="CUDA"):
+        fp4.hadamard(torch.zeros(4, 256), 128)
+    with pytest.raises(ValueError, match="CUDA"):
+        fp4.quantize(torch.zeros(4, 256), p)
+    short = fp4.QTensor(torch.zeros(64 * 128 - 1, dtype=torch.uint8), a.scales, None, 64, 256, p)
+    with pytest.raises(ValueError, match="at least 8192 bytes"):
+        fp4._check_q(short, 64, 256, p, torch.device("cpu"), "q")
