@@ -232,6 +232,7 @@ def quantize(x: torch.Tensor, params: Params = MXFP4, out: QTensor | None = None
                             workspace.data_ptr() if workspace is not None else None, wsb,
                             _stream_ptr(x.device))
     _check(st, "fp4_quantize")
+    q.rows, q.cols, q.params = rows, cols, params  # a reused out now describes this tensor
     return q
 
 
@@ -263,6 +264,8 @@ def quantize_batch(xs, params: Params = MXFP4, outs=None, tensor_scales=None) ->
     p = params.c()
     st = lib().fp4_quantize_batch(n, items, _dtype_code(xs[0]), ctypes.byref(p), _stream_ptr(xs[0].device))
     _check(st, "fp4_quantize_batch")
+    for q, x in zip(qs, xs):
+        q.rows, q.cols, q.params = x.shape[0], x.shape[1], params
     return qs
 
 
@@ -290,6 +293,7 @@ def quantize_colwise(x: torch.Tensor, params: Params = MXFP4, out: QTensor | Non
                                     workspace.data_ptr() if workspace is not None else None, wsb,
                                     _stream_ptr(x.device))
     _check(st, "fp4_quantize_colwise")
+    q.rows, q.cols, q.params = cols, rows, params
     return q
 
 
@@ -375,6 +379,7 @@ def gemm(a: QTensor, b: QTensor, out_dtype=torch.bfloat16, out: torch.Tensor | N
                         _ws_bytes(workspace, wb, dev), _stream_ptr(dev))
     _check(st, "fp4_gemm")
     if out_q is not None:
+        q_out.rows, q_out.cols, q_out.params, q_out.tensor_scale = a.rows, b.rows, out_q, None
         return c, q_out
     return c
 
