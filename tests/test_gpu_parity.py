@@ -605,3 +605,28 @@ def test_gemm_into_a_column_block(M, N, K, kind, c_dtype):
     wide = torch.zeros((M, N + 8), dtype=c_dtype, device=DEV)
     with pytest.raises(fp4.Fp4Error):
         fp4.gemm(qa, qb, out=wide[:, 1:N + 1])
+
+
+def test_reused_outputs_describe_what_was_written(orc):
+    """An output QTensor allocated for other params (same buffer sizes) and reused: after the call
+    it carries the params and shape of what was written, and those codes equal the oracle's."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((96, 256)).astype(np.float32)
+    p_old, p_new = P(scale_mode=CEIL), P(hadamard_n=64, round_mode=SR, seed=5)
+    q = fp4.empty_qtensor(96, 256, p_old, DEV)
+    got = fp4.quantize(_to_dev(x), p_new, out=q)
+    torch.cuda.synchronize()
+    assert got is q and q.params == p_new and (q.rows, q.cols) == (96, 256)
+    oc, os_, _ = _orc_quant(orc, x, p_new)
+    assert np.array_equal(q.codes.cpu().numpy(), oc.reshape(-1))
+    assert np.array_equal(q.scales.cpu().numpy(), os_.reshape(-1).view(np.uint8))
+    # the fused output quantize fills a C_q allocated for another rule
+    w = (rng.standard_normal((64, 256)) * 0.05).astype(np.float32)
+    qa, qb = fp4.quantize(_to_dev(x), P()), fp4.quantize(_to_dev(w), P())
+    oq = P(scale_mode=CEIL)
+    cq = fp4.empty_qtensor(96, 64, P(), DEV)
+    c, cq2 = fp4.gemm(qa, qb, out_dtype=torch.float32, out_q=oq, q_out=cq)
+    torch.cuda.synchronize()
+    assert cq2 is cq and cq.params == oq and (cq.rows, cq.cols) == (96, 64)
+    oc, os_, _ = _orc_quant(orc, c.cpu().numpy(), oq)
+    assert np.array_equal(cq.codes.cpu().numpy(), oc.reshape(-1))
