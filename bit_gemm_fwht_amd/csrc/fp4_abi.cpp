@@ -485,4 +485,25 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
     }
 }
 
+int fp4_nvfp4_to_mxfp8(const void* codes, const void* scales, int64_t rows, int64_t cols, void* out_codes,
+                       void* out_scales, void* stream) {
+    try {
+        if (!codes || !scales || !out_codes || !out_scales || rows <= 0 || cols <= 0) return FP4_ERR_INVALID_ARG;
+        if (cols % 32) return FP4_ERR_INVALID_ARG;
+        if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(out_codes, 16)) return FP4_ERR_ALIGNMENT;
+        const void* ins[2] = {codes, scales};
+        for (const void* p : ins)
+            if (p == out_codes || p == out_scales) return FP4_ERR_INVALID_ARG;
+        if (out_codes == out_scales) return FP4_ERR_INVALID_ARG;
+        if (rows * (cols / 32) >= (int64_t(1) << 39)) return FP4_ERR_UNSUPPORTED;  // grid size
+        return hip_status(launch_nv_to_fp8(reinterpret_cast<const uint8_t*>(codes),
+                                           reinterpret_cast<const uint8_t*>(scales), rows, cols,
+                                           reinterpret_cast<uint8_t*>(out_codes),
+                                           reinterpret_cast<uint8_t*>(out_scales),
+                                           reinterpret_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return FP4_ERR_INTERNAL;
+    }
+}
+
 }  // extern "C"

@@ -96,6 +96,10 @@ struct GemmArgs {
     uint8_t* sb8;
 };
 
+// NVFP4 [rows, cols] -> E4M3 [rows, cols] + E8M0 [rows, cols / 32] (the GEMM's FP8 re-expression)
+hipError_t launch_nv_to_fp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                            uint8_t* out, uint8_t* out_scales, hipStream_t s);
+
 // kind: 0 MXFP4, 1 MXFP8, 2 NVFP4 (via the FP8 rescale)
 hipError_t launch_gemm(const GemmArgs& g, int kind, int c_dtype, int fused_q, hipStream_t s);
 

@@ -753,6 +753,14 @@ __global__ __launch_bounds__(256) void k_nv_to_fp8(NvPair pr) {
     dst[1] = (u32x4){o[4], o[5], o[6], o[7]};
 }
 
+hipError_t launch_nv_to_fp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                            uint8_t* out, uint8_t* out_scales, hipStream_t s) {
+    const int64_t groups = rows * (cols / 32);
+    NvPair pr{{codes, codes}, {scales, scales}, {out, out}, {out_scales, out_scales}, {groups, 0}};
+    hipLaunchKernelGGL(k_nv_to_fp8, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, pr);
+    return hipGetLastError();
+}
+
 template <bool FP8, bool B2D, bool NVG, int FQ>
 static hipError_t launch_out(const GemmArgs& g, int c_dtype, hipStream_t s) {
     const int64_t rowb = FP8 ? g.K : g.K / 2;

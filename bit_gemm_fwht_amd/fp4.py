@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
     L.fp4_gemm_workspace_bytes.restype = I64
     L.fp4_gemm.argtypes = [QT, QT, P, I32, I64, QP, QT, P, I64, P]
     L.fp4_gemm.restype = ctypes.c_int
+    L.fp4_nvfp4_to_mxfp8.argtypes = [P, P, I64, I64, P, P, P]
+    L.fp4_nvfp4_to_mxfp8.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -382,6 +384,24 @@ def gemm(a: QTensor, b: QTensor, out_dtype=torch.bfloat16, out: torch.Tensor | N
         q_out.rows, q_out.cols, q_out.params, q_out.tensor_scale = a.rows, b.rows, out_q, None
         return c, q_out
     return c
+
+
+def nvfp4_to_mxfp8(q: QTensor) -> QTensor:
+    """The FP8 re-expression of an NVFP4 tensor (E4M3 elements, one E8M0 scale per 32 along the
+    rows), the operand form the GEMM multiplies NVFP4 operands in. The result's tensor_scale is q's
+    (it still multiplies the product)."""
+    if q.params.scale_mode not in NV_MODES:
+        raise ValueError("nvfp4_to_mxfp8 takes an NVFP4 tensor")
+    dev = q.codes.device
+    _check_q(q, q.rows, q.cols, q.params, dev, "q")
+    p8 = Params(elem=E4M3, block=(1, 32), scale_mode=SCALE_E8M0_FLOOR)
+    cb, sb, _ = buffer_sizes(q.rows, q.cols, p8)
+    codes = torch.empty(cb, dtype=torch.uint8, device=dev)
+    scales = torch.empty(sb, dtype=torch.uint8, device=dev)
+    st = lib().fp4_nvfp4_to_mxfp8(q.codes.data_ptr(), q.scales.data_ptr(), q.rows, q.cols, codes.data_ptr(),
+                                  scales.data_ptr(), _stream_ptr(dev))
+    _check(st, "fp4_nvfp4_to_mxfp8")
+    return QTensor(codes, scales, q.tensor_scale, q.rows, q.cols, p8)
 
 
 def upload_qtensor(codes, scales, tensor_scale, rows, cols, params: Params, device) -> QTensor:

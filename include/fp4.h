@@ -211,6 +211,19 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
              const fp4_qparams* out_q, fp4_qtensor* C_q, void* workspace, int64_t ws_bytes,
              void* stream);
 
+/* The FP8 re-expression of an NVFP4 tensor, the operand form the GEMM multiplies NVFP4 x NVFP4 in
+ * (the gfx950 scaled matrix instructions take one power-of-two scale per 32 K values): codes
+ * (E2M1 [rows, cols/2]) and scales (E4M3 [rows, cols/16], the (1, 16) blocks of the NVFP4 modes of
+ * "Four Over Six: More Accurate NVFP4 Quantization with Adaptive Block Scaling", methodology) become
+ * out_codes (E4M3 [rows, cols]) and out_scales (E8M0 [rows, cols/32]): per 32-wide group, with S the
+ * larger of its two block scales, E is the smallest exponent with 448 * 2^E >= 6 S (E = -127 when
+ * S = 0, code E + 127) and each element is E4M3(val(q) * s_blk * 2^-E), nearest even (lossy: the
+ * product of a 2-bit element and a 4-bit scale can need 6 significant bits). The fp32 tensor scale
+ * is not involved (it multiplies the GEMM's result). Requirements: cols % 32 == 0; codes and
+ * out_codes 16-byte aligned, scales 2-byte aligned; outputs must not alias the inputs. */
+int fp4_nvfp4_to_mxfp8(const void* codes, const void* scales, int64_t rows, int64_t cols, void* out_codes,
+                       void* out_scales, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.orc_dequantize.restype = _INT
     L.orc_operand_f64.argtypes = [_P, _P, _P, _I64, _I64, _INT, _INT, _INT, _INT, _INT, _P]
     L.orc_operand_f64.restype = _INT
+    L.orc_nv_to_mx8.argtypes = [_P, _P, _I64, _I64, _INT, _P, _P]
+    L.orc_nv_to_mx8.restype = _INT
     L.orc_gemm_f64.argtypes = [_P, _P, _I64, _I64, _I64, _P, _P]
     L.orc_gemm_f64.restype = None
     L.orc_gemm_f64_sampled.argtypes = [_P, _P, _I64, _P, _P, _I64, _P, _P]
@@ -216,6 +218,18 @@ def operand_f64(codes, scales, tensor_scale, rows, K, *, elem=E2M1, block=(1, 32
     if rc:
         raise ValueError(f"orc_operand_f64 rejected the arguments (code {rc})")
     return out
+
+
+def nv_to_mx8(codes, scales, rows, K, block_cols=16):
+    """The FP8 re-expression of an NVFP4 operand: (E4M3 codes [rows, K], E8M0 codes [rows, K/32])."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    f8 = np.empty((rows, K), dtype=np.uint8)
+    e8 = np.empty((rows, K // 32), dtype=np.uint8)
+    rc = lib().orc_nv_to_mx8(_ptr(codes), _ptr(scales), rows, K, block_cols, _ptr(f8), _ptr(e8))
+    if rc:
+        raise ValueError(f"orc_nv_to_mx8 rejected the arguments (code {rc})")
+    return f8, e8
 
 
 def gemm_f64(a, b):

@@ -465,28 +465,63 @@ int orc_operand_f64(const uint8_t* codes, const void* scales, const float* tenso
             }
         return 0;
     }
-    /* NVFP4 on a matrix core that takes one power-of-two scale per 32 K values: per 32-wide K
-     * group take S = the larger of its E4M3 block scales, E = the smallest exponent with
-     * 448 * 2^E >= 6 S, and re-encode each element as f = E4M3(val(q) * s_blk * 2^-E) (RNE). The
-     * value the product sees is val(f) * 2^E * g. */
+    /* NVFP4 on a matrix core that takes one power-of-two scale per 32 K values: the operand is
+     * first re-expressed as E4M3 elements with one E8M0 exponent per 32-wide K group
+     * (orc_nv_to_mx8); the value the product sees is val(f) * 2^E * g. */
     if (K % 32 || 32 % block_cols) return -10;
+    uint8_t* f8 = (uint8_t*)malloc((size_t)(rows * K));
+    uint8_t* e8 = (uint8_t*)malloc((size_t)(rows * (K / 32)));
+    if (!f8 || !e8) {
+        free(f8);
+        free(e8);
+        return -100;
+    }
+    rc = orc_nv_to_mx8(codes, scales, rows, K, block_cols, f8, e8);
+    if (rc) {
+        free(f8);
+        free(e8);
+        return rc;
+    }
     const double g = (double)(tensor_scale ? *tensor_scale : 1.0f);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < K; ++k) {
+            int E = (int)e8[r * (K / 32) + k / 32] - 127;
+            out[r * K + k] = (double)orc_e4m3_value(f8[r * K + k]) * ldexp(1.0, E) * g;
+        }
+    free(f8);
+    free(e8);
+    return 0;
+}
+
+/* The re-expression of an NVFP4 operand (E2M1 codes with one E4M3 scale per block_cols-wide block,
+ * block_cols dividing 32) as E4M3 elements with one power-of-two (E8M0) scale per 32-wide K group,
+ * the operand form of a matrix core that takes only power-of-two block scales. Per group: S = the
+ * largest of its E4M3 block scales; E = the smallest exponent with 448 * 2^E >= 6 S, so that every
+ * |val(q) * s_blk| <= 6 S fits below 448 * 2^E (E = -127 when S = 0); each element becomes
+ * f = E4M3(val(q) * s_blk * 2^-E), nearest even. val(q) * s_blk is exact in fp32 (2 and 4
+ * significant bits) and so is the scaling by 2^-E; the E4M3 rounding is the one lossy step. The
+ * tensor scale g is not part of it (it multiplies the whole product). Out: E4M3 codes [rows, K],
+ * E8M0 codes E + 127 [rows, K / 32]. */
+int orc_nv_to_mx8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K,
+                  int block_cols, uint8_t* out_codes, uint8_t* out_scales) {
+    if (rows <= 0 || K <= 0 || K % 32 || block_cols <= 0 || 32 % block_cols) return -10;
+    const int64_t nbc = K / block_cols;
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t k0 = 0; k0 < K; k0 += 32) {
             float S = 0.0f;
             for (int64_t k = k0; k < k0 + 32; k += block_cols)
-                S = fmaxf(S, orc_e4m3_value(((const uint8_t*)scales)[r * nbc + k / block_cols]));
+                S = fmaxf(S, orc_e4m3_value(scales[r * nbc + k / block_cols]));
             int E = -127;
             if (S > 0.0f) {
                 E = -40;
                 while (ldexp(448.0, E) < 6.0 * (double)S) ++E;
             }
+            out_scales[r * (K / 32) + k0 / 32] = (uint8_t)(E + 127);
             for (int64_t k = k0; k < k0 + 32; ++k) {
-                float s_blk = orc_e4m3_value(((const uint8_t*)scales)[r * nbc + k / block_cols]);
-                float t = orc_e2m1_value(get_code(codes, elem, K, r, k)) * s_blk;
+                float s_blk = orc_e4m3_value(scales[r * nbc + k / block_cols]);
+                float t = orc_e2m1_value(get_code(codes, ORC_ELEM_E2M1, K, r, k)) * s_blk;
                 t = ldexpf(t, -E);
-                uint8_t f = orc_e4m3_rne(t);
-                out[r * K + k] = (double)orc_e4m3_value(f) * ldexp(1.0, E) * g;
+                out_codes[r * K + k] = orc_e4m3_rne(t);
             }
         }
     return 0;

@@ -98,6 +98,14 @@ int orc_operand_f64(const uint8_t* codes, const void* scales, const float* tenso
                     int64_t rows, int64_t K, int elem, int block_rows, int block_cols,
                     int scale_mode, int with_nv_exact, double* out);
 
+/* The FP8 re-expression of an NVFP4 operand (E2M1 codes [rows, K/2], E4M3 block scales
+ * [rows, K/block_cols], block_cols dividing 32): per 32-wide K group, E = the smallest exponent with
+ * 448 * 2^E >= 6 S (S the group's largest block scale; E = -127 when S = 0) and elements
+ * f = E4M3(val(q) * s_blk * 2^-E), nearest even. out_codes: E4M3 [rows, K]; out_scales: E8M0
+ * codes E + 127 [rows, K/32]. */
+int orc_nv_to_mx8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K,
+                  int block_cols, uint8_t* out_codes, uint8_t* out_scales);
+
 /* C[m,n] = sum_k a[m,k] * b[n,k] in fp64 and S[m,n] = sum_k |a[m,k] b[n,k]| (the error scale).
  * Full or at (ms[i], ns[i]) pairs. */
 void orc_gemm_f64(const double* a, const double* b, int64_t M, int64_t N, int64_t K,

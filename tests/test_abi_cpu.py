@@ -274,3 +274,24 @@ def test_binding_refuses_host_and_undersized_buffers(fp4):
     short = fp4.QTensor(torch.zeros(64 * 128 - 1, dtype=torch.uint8), a.scales, None, 64, 256, p)
     with pytest.raises(ValueError, match="at least 8192 bytes"):
         fp4._check_q(short, 64, 256, p, torch.device("cpu"), "q")
+
+
+def test_nvfp4_to_mxfp8_rejects_bad_arguments(fp4):
+    """Host-side checks of the re-expression entry point (nothing reaches the device)."""
+    L = fp4.lib()
+    E = fp4
+    good = dict(codes=0x10000, scales=0x20000, rows=8, cols=64, oc=0x30000, os=0x40000)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return L.fp4_nvfp4_to_mxfp8(a["codes"], a["scales"], a["rows"], a["cols"], a["oc"], a["os"], None)
+
+    assert call(codes=None) == E.ERR_INVALID_ARG
+    assert call(os=None) == E.ERR_INVALID_ARG
+    assert call(rows=0) == E.ERR_INVALID_ARG
+    assert call(cols=48) == E.ERR_INVALID_ARG        # cols % 32
+    assert call(codes=0x10008) == E.ERR_ALIGNMENT     # codes need 16 bytes
+    assert call(scales=0x20001) == E.ERR_ALIGNMENT    # scales need 2 bytes
+    assert call(oc=0x30004) == E.ERR_ALIGNMENT
+    assert call(oc=0x10000) == E.ERR_INVALID_ARG      # output aliases an input
+    assert call(os=0x30000) == E.ERR_INVALID_ARG      # outputs alias each other

@@ -1,0 +1,221 @@
+"""The NVFP4 -> MXFP8 re-expression on the GPU, byte for byte against the oracle: the standalone
+conversion (fp4_nvfp4_to_mxfp8) and the copy the GEMM writes into its workspace before it runs the
+FP8 matrix cores. Per 32-wide K group: E = the smallest exponent with 448 * 2^E >= 6 S (S the larger
+block scale) and elements E4M3(val(q) * s_blk * 2^-E), nearest even."""
+import numpy as np
+import pytest
+import torch
+
+from bit_gemm_fwht_amd import fp4
+from bit_gemm_fwht_amd import workloads as wl
+from test_gpu_parity import NV, NV46, P, _orc_quant, _to_dev
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _random_nv(rows, cols, seed):
+    """E2M1 codes (every byte value) and E4M3 block scales over the whole finite range, with all-zero
+    groups, E4M3 subnormal scales and the largest scale planted."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, size=(rows, cols // 16), dtype=np.uint8)
+    scales[0, :4] = 0
+    scales[1, :2] = [1, 7]
+    scales[2, :2] = [0x7E, 0x7E]
+    scales[3, :2] = [0x08, 0x01]
+    scales[4, :] = rng.integers(0, 8, size=cols // 16)  # a row of subnormal scales
+    return codes, scales
+
+
+def _convert(codes, scales, rows, cols, params=None):
+    q = fp4.upload_qtensor(codes, scales, np.float32([1.0]), rows, cols,
+                           params or P(block=(1, 16), scale_mode=NV), DEV)
+    q8 = fp4.nvfp4_to_mxfp8(q)
+    torch.cuda.synchronize()
+    return q8.codes.cpu().numpy().reshape(rows, cols), q8.scales.cpu().numpy().reshape(rows, cols // 32)
+
+
+@pytest.mark.parametrize("rows,cols,seed", [(37, 512, 0), (1, 32, 1), (256, 1024, 2), (5, 96, 3)])
+def test_nvfp4_to_mxfp8_matches_oracle(orc, rows, cols, seed):
+    codes, scales = _random_nv(max(rows, 5), cols, seed)
+    codes, scales = codes[:rows], scales[:rows]
+    f8, e8 = _convert(codes, scales, rows, cols)
+    of8, oe8 = orc.nv_to_mx8(codes, scales, rows, cols)
+    assert np.array_equal(e8, oe8), f"{np.sum(e8 != oe8)} E8M0 scale bytes differ"
+    bad = np.argwhere(f8 != of8)
+    assert bad.size == 0, f"{len(bad)} E4M3 bytes differ, first {bad[:4].tolist()}: gpu {f8[tuple(bad[0])]} oracle {of8[tuple(bad[0])]}"
+
+
+def test_nvfp4_to_mxfp8_of_quantized_tensor(orc):
+    """On an NVFP4 + 4/6 quantization of Laplace data with outliers (the 8192^3 workload's
+    distribution, 256 x 1024)."""
+    x, _ = wl.nvfp4_4over6(0, m=256, n=16, k=1024)
+    p = P(block=(1, 16), scale_mode=NV46)
+    oc, os_, ots = _orc_quant(orc, x, p)
+    f8, e8 = _convert(oc, os_, 256, 1024, p)
+    of8, oe8 = orc.nv_to_mx8(oc, os_, 256, 1024)
+    assert np.array_equal(e8, oe8) and np.array_equal(f8, of8)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 520, 384), (64, 96, 128), (512, 256, 1024)])
+def test_gemm_workspace_holds_the_reexpression(orc, M, N, K):
+    """The FP8 operands the NVFP4 GEMM multiplies (its workspace: A's E4M3 codes, A's E8M0 scales,
+    then B's, each region padded to 256 bytes) equal the oracle's re-expression."""
+    rng = np.random.default_rng(M + N + K)
+    A = rng.laplace(size=(M, K)).astype(np.float32)
+    B = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    pa, pb = P(block=(1, 16), scale_mode=NV46), P(block=(1, 16), scale_mode=NV)
+    ca, sa, ta = _orc_quant(orc, A, pa)
+    cb, sb, tb = _orc_quant(orc, B, pb)
+    qa = fp4.upload_qtensor(ca, sa, ta, M, K, pa, DEV)
+    qb = fp4.upload_qtensor(cb, sb, tb, N, K, pb, DEV)
+    wb = fp4.gemm_workspace_bytes(qa, qb)
+    ws = torch.zeros(wb, dtype=torch.uint8, device=DEV)
+    fp4.gemm(qa, qb, out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    w = ws.cpu().numpy()
+
+    def r(n):
+        return (n + 255) // 256 * 256
+
+    o = 0
+    regions = []
+    for n in (M * K, M * K // 32, N * K, N * K // 32):
+        regions.append(w[o:o + n])
+        o += r(n)
+    assert o == wb
+    of8a, oe8a = orc.nv_to_mx8(ca, sa, M, K)
+    of8b, oe8b = orc.nv_to_mx8(cb, sb, N, K)
+    for got, ref, what in zip(regions, (of8a, oe8a, of8b, oe8b), ("A codes", "A scales", "B codes", "B scales")):
+        assert np.array_equal(got, ref.reshape(-1)), f"{what}: {np.sum(got != ref.reshape(-1))} bytes differ"
+
+
+# ---------------------------------------------------------------------------------------------
+# The FP8 matrix core's summation, pinned on crafted operands
+# ---------------------------------------------------------------------------------------------
+def _e4m3_code(v):
+    """E4M3FN code of an exactly representable value (normal or subnormal, |v| <= 448)."""
+    s = 0x80 if v < 0 else 0
+    a = abs(v)
+    if a == 0:
+        return s
+    if a < 2.0**-6:
+        m = a / 2.0**-9
+        assert m == int(m) and 1 <= m <= 7, v
+        return s | int(m)
+    e = int(np.floor(np.log2(a)))
+    m = a / 2.0**e - 1
+    assert -6 <= e <= 8 and m * 8 == int(m * 8) and a <= 448, v
+    return s | ((e + 7) << 3) | int(m * 8)
+
+
+def _alignment_model(a, b):
+    """sum_k a_k b_k as the FP8 matrix core forms it: in each aligned block of 8 consecutive K
+    products, every product is truncated toward zero to a multiple of 2^(e - 13), e the exponent of
+    the block's largest |product|; the block sums are then added exactly (every case below has an
+    fp32-exact total)."""
+    p = (np.asarray(a, dtype=np.float64) * np.asarray(b, dtype=np.float64)).reshape(-1, 8)
+    total = 0.0
+    for blk in p:
+        m = np.abs(blk).max()
+        if m == 0:
+            continue
+        unit = 2.0 ** (np.floor(np.log2(m)) - 13)
+        total += float(np.sum(np.trunc(blk / unit) * unit))
+    return total
+
+
+def _alignment_cases(K):
+    """(A row, B row) pairs of exact values; groups of 32 share one power-of-two scale, chosen so
+    that every element is an E4M3 value."""
+    cases = []
+
+    def add(a, b=None):
+        ra, rb = np.zeros(K), np.ones(K)
+        for k, v in a.items():
+            ra[k] = v
+        for k, v in (b or {}).items():
+            rb[k] = v
+        cases.append((ra, rb))
+
+    for j in range(3, 10):                        # a single small product 2^-11 .. 2^-17 below 256
+        add({0: 256.0, 1: 2.0**-j})
+    for j in (3, 4, 5, 6):                        # 4-bit small products straddling the window
+        add({0: 256.0, 1: 1.875 * 2.0**-j})
+    add({0: 256.0, 1: -1.875 * 2.0**-4})          # negative small: truncated toward zero
+    add({0: -256.0, 1: 1.875 * 2.0**-4})
+    add({0: -256.0, 1: -1.875 * 2.0**-4})
+    add({0: 448.0, 1: 1.875 * 2.0**-4})           # largest product not a power of two
+    add({0: 256.0, **{k: 2.0**-6 for k in range(1, 8)}})        # truncated one by one, not summed first
+    add({0: 256.0, **{k: 1.875 * 2.0**-4 for k in range(1, 8)}})
+    add({0: 256.0, 8: 2.0**-8})                   # next block of 8: exact
+    add({4: 256.0, **{k: 2.0**-8 for k in list(range(0, 4)) + list(range(5, 16))}})
+    add({0: 256.0, 1: 1.875 * 2.0**-4}, {1: 1.875})  # an 8-bit product truncated
+    add({0: 16.0, 1: 1.875 * 2.0**-4}, {0: 16.0})    # the largest product from both operands
+    add({0: 1.0, **{k: 2.0**-14 for k in range(32, 64)}})  # other 32-group (own scale): exact
+    add({0: 1.0, **{k: 2.0**-14 for k in range(1, 64)}})   # 7 lost in the first block only
+    add({0: 2.0, **{k: 2.0**-9 for k in range(1, 8)}})
+    return cases
+
+
+def _encode_rows(rows, K):
+    codes = np.zeros((len(rows), K), dtype=np.uint8)
+    scales = np.full((len(rows), K // 32), 127, dtype=np.uint8)
+    for i, r in enumerate(rows):
+        for g in range(K // 32):
+            blk = r[32 * g:32 * g + 32]
+            mx = np.abs(blk).max()
+            k = 0 if mx == 0 else int(np.floor(np.log2(mx))) - 8  # largest element in [256, 512)
+            if mx / 2.0**k > 448:
+                k += 1
+            scales[i, g] = k + 127
+            codes[i, 32 * g:32 * g + 32] = [_e4m3_code(v / 2.0**k) for v in blk]
+    return codes, scales
+
+
+@pytest.mark.parametrize("MN", [256, 64])  # the 256x256-tile kernel (32x32x64) and the small one (16x16x128)
+def test_fp8_matrix_core_alignment_model(MN):
+    """MXFP8 products on the matrix core equal the alignment model exactly on crafted rows: a
+    dominant product and small ones in one aligned block of 8 lose the bits below 2^(e - 13), toward
+    zero, product by product; products in other blocks of 8 are summed exactly. This is the rule
+    behind the FP8 term of the GEMM bound (fp8_alignment_term)."""
+    K = 128
+    cases = _alignment_cases(K)
+    A = np.zeros((MN, K))
+    B = np.ones((MN, K))
+    for i, (a, b) in enumerate(cases):
+        A[i], B[i] = a, b
+    ca, sa = _encode_rows(A, K)
+    cb, sb = _encode_rows(B, K)
+    p8 = P(elem=fp4.E4M3)
+    qa = fp4.upload_qtensor(ca, sa, None, MN, K, p8, DEV)
+    qb = fp4.upload_qtensor(cb, sb, None, MN, K, p8, DEV)
+    c = fp4.gemm(qa, qb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    c = c.cpu().numpy()
+    lost = 0
+    for i, (a, b) in enumerate(cases):
+        model = _alignment_model(a, b)
+        exact = float(np.dot(a, b))
+        assert np.float32(model) == model  # the cases are fp32-exact
+        assert c[i, i] == np.float32(model), f"case {i}: got {c[i, i]!r}, model {model!r}, exact {exact!r}"
+        lost += model != exact
+    assert lost >= 15  # most cases do lose bits: the exact sum would fail them
+
+
+def test_mxfp4_products_are_summed_exactly():
+    """The same dominant-plus-small pattern in E2M1 (largest 6 * 6, smallest 0.5 * 0.5 within one
+    group) comes back exact: FP4 products of one group never leave the 13-bit window."""
+    K, MN = 128, 256
+    codes = np.zeros((MN, K // 2), dtype=np.uint8)
+    codes[0, 0] = 0x77           # 6, 6
+    codes[0, 1:4] = 0x11         # 0.5 ... in the same block of 8
+    bcodes = np.full((MN, K // 2), 0x77, dtype=np.uint8)  # 6 everywhere
+    bcodes[0, 1:4] = 0x11
+    s = np.full((MN, K // 32), 127, dtype=np.uint8)
+    qa = fp4.upload_qtensor(codes, s, None, MN, K, P(), DEV)
+    qb = fp4.upload_qtensor(bcodes, s, None, MN, K, P(), DEV)
+    c = fp4.gemm(qa, qb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert c[0, 0].item() == 36.0 + 36.0 + 6 * 0.25

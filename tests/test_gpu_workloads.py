@@ -1,13 +1,13 @@
 """Parity at the full sizes of the large workloads, in the configuration bench.py times:
 quantization compared element for element with the oracle (codes and scales bit-exact), GEMM
-outputs compared on a seeded sample of 2048 positions (the oracle computes each one on its own)."""
+outputs compared on a seeded sample of 4096 positions (the oracle computes each one on its own)."""
 import numpy as np
 import pytest
 import torch
 
 from bit_gemm_fwht_amd import fp4
 from bit_gemm_fwht_amd import workloads as wl
-from test_gpu_parity import CEIL, E4M3, NV46, SR, P, _gemm_tol, _orc_quant, _to_dev
+from test_gpu_parity import CEIL, E4M3, NV46, SR, P, _gemm_tol, _orc_quant, _to_dev, report_ratio
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -24,7 +24,7 @@ def _quant_both(orc, x, params):
     return q, (oc, os_, ots)
 
 
-def _sampled_gemm(orc, qa, qb, oa, ob, pa, pb, c_dtype, n=2048, seed=0):
+def _sampled_gemm(orc, qa, qb, oa, ob, pa, pb, c_dtype, n=4096, seed=0):
     c = fp4.gemm(qa, qb, out_dtype=c_dtype)
     torch.cuda.synchronize()
     M, N, K = qa.rows, qb.rows, qa.cols
@@ -47,6 +47,7 @@ def _sampled_gemm(orc, qa, qb, oa, ob, pa, pb, c_dtype, n=2048, seed=0):
     ref, sabs = orc.gemm_f64_sampled(a64, b64, im, inn)
     tol = _gemm_tol(ref, sabs, a64, b64, im, inn, pa, K, c_dtype)
     err = np.abs(got - ref)
+    report_ratio(err, ref, sabs, c_dtype, f"{M}x{N}x{K} {pa.elem}/{pa.scale_mode} sampled {n}")
     assert np.all(err <= tol), f"{np.sum(err > tol)} of {n} sampled outputs exceed the bound"
 
 

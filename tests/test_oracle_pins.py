@@ -161,6 +161,29 @@ def test_e4m3_saturates(orc):
     assert orc.encode(v, orc.E4M3).tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0x7E]
 
 
+def test_bf16_rne_matches_torch(orc):
+    """fp32 -> bf16 (round to nearest even) against torch's CPU cast: every fp32 high half (sign,
+    exponent, top mantissa bits, so every binade incl. subnormals, +-0 and values near FLT_MAX) with
+    the low halves that decide the rounding (0, 1, just below / at / just above the tie, all ones),
+    plus 2^22 random fp32 patterns. NaN inputs are checked to stay NaN (payloads are free)."""
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x4000, 0xC000], dtype=np.uint32)
+    rng = np.random.default_rng(21)
+    u = np.concatenate([(hi[:, None] | lows[None, :]).ravel(),
+                        rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)])
+    v = u.view(np.float32)
+    got = orc.bf16_rne(v)
+    ref = torch.from_numpy(v.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(v)
+    assert np.array_equal(got[~nan], ref[~nan])
+    g32 = (got[nan].astype(np.uint32) << 16).view(np.float32)
+    assert np.all(np.isnan(g32))
+    # ties go to the even bf16 mantissa; values past the largest bf16 round to infinity
+    assert orc.bf16_rne(np.float32([1.0 + 2.0**-8]))[0] == 0x3F80
+    assert orc.bf16_rne(np.float32([1.0 + 3 * 2.0**-8]))[0] == 0x3F82
+    assert orc.bf16_rne(np.float32([3.4028235e38]))[0] == 0x7F80
+
+
 def test_e8m0_decode_matches_torch(orc):
     codes = np.arange(255, dtype=np.uint8)
     ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).float().numpy()
@@ -520,14 +543,69 @@ def test_nvfp4_fp8_rescale_is_exact_when_scales_are_powers_of_two(orc):
     b = orc.operand_f64(codes, scales, ts, rows, K, block=(1, 16), scale_mode=orc.SCALE_NV,
                         nv_exact=True)
     assert np.array_equal(a, b)
-    # general scales: the per-element relative change is at most half an E4M3 ulp (2^-4)
-    scales = rng.integers(1, 0x7E, size=(rows, K // 16), dtype=np.uint8)
+
+
+def _e2m1_exact(code):
+    """E2M1 value of a code as an exact fraction, from the grid the page prints."""
+    mag = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+           Fraction(4), Fraction(6)][code & 7]
+    return -mag if code & 8 else mag
+
+
+def _e4m3_exact(code):
+    """E4M3FN value (finite codes) as an exact fraction: bias 7, subnormal step 2^-9."""
+    e, m = (code >> 3) & 15, code & 7
+    v = Fraction(m, 512) if e == 0 else Fraction(8 + m, 8) * Fraction(2) ** (e - 7)
+    return -v if code & 0x80 else v
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_nvfp4_fp8_rescale_rule(orc, seed):
+    """The re-expression NVFP4 -> E4M3 elements under one power-of-two scale per 32-wide K group,
+    checked in exact arithmetic: per group, 448 * 2^E >= 6 S > 448 * 2^(E-1) (E is the smallest
+    such exponent; S the group's larger block scale), E = -127 for S = 0, and every element is the
+    E4M3 nearest-even rounding (torch's float8_e4m3fn cast) of the exact val(q) * s_blk * 2^-E.
+    Scale codes cover E4M3 subnormals, zero and the largest code; an E one too large or too small,
+    a swapped block scale or another rounding fails here."""
+    rng = np.random.default_rng(100 + seed)
+    rows, K = 24, 256
+    codes = rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, size=(rows, K // 16), dtype=np.uint8)  # 0x00 .. 0x7E
+    scales[0, :4] = 0                      # two all-zero groups
+    scales[1, :2] = [1, 2]                 # subnormal block scales
+    scales[2, :2] = [0x7E, 0x7E]           # the largest scale
+    scales[3, :2] = [0x08, 0x01]           # 2^-6 next to the smallest subnormal
+    f8, e8 = orc.nv_to_mx8(codes, scales, rows, K)
+    nib = np.empty((rows, K), dtype=np.uint8)
+    nib[:, 0::2] = codes & 0xF
+    nib[:, 1::2] = codes >> 4
+    two = Fraction(2)
+    for r in range(rows):
+        for g in range(K // 32):
+            s = [_e4m3_exact(int(scales[r, 2 * g])), _e4m3_exact(int(scales[r, 2 * g + 1]))]
+            S = max(s)
+            E = int(e8[r, g]) - 127
+            if S == 0:
+                assert E == -127
+            else:
+                assert 448 * two ** E >= 6 * S > 448 * two ** (E - 1), (r, g, E, S)
+            args = []
+            for j in range(32):
+                t = _e2m1_exact(int(nib[r, 32 * g + j])) * s[j // 16] * two ** (-E)
+                assert abs(t) <= 448
+                tf = np.float32(float(t))
+                assert Fraction(float(tf)) == t  # the argument is exact in fp32
+                if t == 0 and nib[r, 32 * g + j] & 8:
+                    tf = np.float32(-0.0)
+                args.append(tf)
+            ref = torch.from_numpy(np.array(args, dtype=np.float32)).to(torch.float8_e4m3fn)
+            ref = ref.view(torch.uint8).numpy()
+            assert np.array_equal(f8[r, 32 * g:32 * g + 32], ref), (r, g)
+    # the GEMM reference multiplies exactly these values
+    ts = np.float32([0.375])
     a = orc.operand_f64(codes, scales, ts, rows, K, block=(1, 16), scale_mode=orc.SCALE_NV)
-    b = orc.operand_f64(codes, scales, ts, rows, K, block=(1, 16), scale_mode=orc.SCALE_NV,
-                        nv_exact=True)
-    nz = b != 0
-    big = np.abs(a[nz]) >= 2.0 ** -6 * 0  # normal-range results
-    assert np.all(np.abs(a[nz] - b[nz])[big] <= np.abs(b[nz])[big] * 2.0**-4 + 2.0**-9 * 64 * 0.75)
+    e4 = torch.from_numpy(f8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(a, e4 * np.repeat(2.0 ** (e8.astype(np.float64) - 127), 32, axis=1) * 0.375)
 
 
 # ---------------------------------------------------------------------------------------------
