@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "fp4_internal.h"
 
@@ -73,6 +74,29 @@ int64_t ws_bytes_needed(Layout lay, const fp4_qparams* p) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_ERR_HIP; }
+
+// Library-owned device scratch of fp4_quantize_noalloc: one copy per GPU, alive until the process
+// ends. Host code never passes `scratch` itself to a kernel (in host code the name is a host-side
+// stand-in, not a device address): the device address is looked up once per device with that device
+// current and kept in scratch_ptr.
+__device__ __attribute__((aligned(256))) uint8_t scratch[FP4_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FP4_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FP4_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FP4_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return FP4_OK;
+}
 
 }  // namespace
 
@@ -176,6 +200,25 @@ int fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int
             if ((rc = hip_status(launch_amax_rows(x, x_dtype, rows, cols, ldx, ws, s))) != FP4_OK) return rc;
         }
         return hip_status(launch_rowblock(a, x_dtype, p->elem, sc, p->round_mode, s));
+    } catch (...) {
+        return FP4_ERR_INTERNAL;
+    }
+}
+
+int fp4_quantize_noalloc(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                         const fp4_qparams* p, void* codes, void* scales, float* tensor_scale, void* stream) {
+    try {
+        Layout lay;
+        const int rc = check_params(rows, cols, p, &lay);
+        if (rc != FP4_OK) return rc;
+        const int64_t need = ws_bytes_needed(lay, p);
+        if (need > FP4_NOALLOC_SCRATCH_BYTES) return FP4_ERR_WORKSPACE;
+        void* ws = nullptr;
+        if (need) {
+            const int s = scratch_for_current_device(&ws);
+            if (s != FP4_OK) return s;
+        }
+        return fp4_quantize(x, x_dtype, rows, cols, ldx, p, codes, scales, tensor_scale, ws, need, stream);
     } catch (...) {
         return FP4_ERR_INTERNAL;
     }

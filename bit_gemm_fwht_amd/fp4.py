@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
     L.fp4_gemm_workspace_bytes.restype = I64
     L.fp4_gemm.argtypes = [QT, QT, P, I32, I64, QP, QT, P, I64, P]
     L.fp4_gemm.restype = ctypes.c_int
+    L.fp4_quantize_noalloc.argtypes = [P, I32, I64, I64, I64, QP, P, P, P, P]
+    L.fp4_quantize_noalloc.restype = ctypes.c_int
     L.fp4_nvfp4_to_mxfp8.argtypes = [P, P, I64, I64, P, P, P]
     L.fp4_nvfp4_to_mxfp8.restype = ctypes.c_int
     _lib = L
@@ -236,6 +238,23 @@ def quantize(x: torch.Tensor, params: Params = MXFP4, out: QTensor | None = None
     _check(st, "fp4_quantize")
     q.rows, q.cols, q.params = rows, cols, params  # a reused out now describes this tensor
     return q
+
+
+def quantize_noalloc(x: torch.Tensor, params: Params, out: QTensor, tensor_scale=None) -> QTensor:
+    """fp4_quantize_noalloc: quantize into the preallocated `out` with no device allocation at all (the
+    tensor-amax scratch is the library's static per-GPU array; overlapping calls on one GPU race)."""
+    if x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D CUDA tensor, contiguous along its last axis")
+    rows, cols = x.shape
+    _check_q(out, rows, cols, params, x.device, "out")
+    _set_given_scale(out, params, tensor_scale)
+    p = params.c()
+    ts = out.tensor_scale.data_ptr() if out.tensor_scale is not None else None
+    st = lib().fp4_quantize_noalloc(x.data_ptr(), _dtype_code(x), rows, cols, x.stride(0), ctypes.byref(p),
+                                    out.codes.data_ptr(), out.scales.data_ptr(), ts, _stream_ptr(x.device))
+    _check(st, "fp4_quantize_noalloc")
+    out.rows, out.cols, out.params = rows, cols, params
+    return out
 
 
 def quantize_batch(xs, params: Params = MXFP4, outs=None, tensor_scales=None) -> list:

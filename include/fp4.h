@@ -140,6 +140,21 @@ int fp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int
                  const fp4_qparams* p, void* codes, void* scales, float* tensor_scale,
                  void* workspace, int64_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc): fp4_quantize without a workspace argument. The scratch the
+ * tensor-wide amax needs (NVFP4 and 4/6 without a given tensor scale, per-tensor blocks) is taken
+ * from a static device array of the library, FP4_NOALLOC_SCRATCH_BYTES per GPU, held by each GPU
+ * the library runs on until the process ends. This call allocates nothing (no hipMalloc, no
+ * allocating library routine); its first call on a device looks up that device's copy of the array.
+ * The word it uses is cleared by a kernel before each use. Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (e.g. on two streams) race on it and must be
+ * serialised by the caller. Arguments, results and errors as for fp4_quantize; a mode whose
+ * workspace exceeds the array returns FP4_ERR_WORKSPACE (none does today: fp4_workspace_bytes is at
+ * most 256). */
+#define FP4_NOALLOC_SCRATCH_BYTES 256
+int fp4_quantize_noalloc(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                         const fp4_qparams* p, void* codes, void* scales, float* tensor_scale, void* stream);
+
 /* One tensor of a batched quantize: x [rows, cols] with leading dimension ldx, its codes, scales
  * and tensor_scale (an input, the tensor scale g, in the _GIVEN NVFP4 modes; else unused). */
 typedef struct {
