@@ -20,6 +20,12 @@ and three that measure extensions of the path:
   backward_dw_colwise dW = dY^T X over 8192 tokens (4096 x 4096 x 8192): dY and X as stored
                      [tokens, features], quantized column-wise (along tokens, H_128, E8M0 ceil;
                      dY with Philox SR) without forming the transposes
+and the two small, launch-latency-bound workloads (reported in microseconds):
+  tiny_mxfp4         A, B fp32 256x256, A's largest entry x50: MXFP4 quantize of both, the 256^3
+                     GEMM (fp32 out) and A's per-tensor fp32-scale quantize (the outlier collapse)
+  mnist_mlp          MNIST-MLP-shaped fp32 weights (256x784, 128x256, 10x128), clean and with a 50x
+                     outlier in fc1: every per-tensor / per-row / group-32 x fp32 / E8M0 floor / E8M0
+                     ceil quantization, with the MSE of each (quantize-only)
 Inputs are resident in HBM before timing starts; the step cycles over several copies of the inputs
 (more than the 256 MB last-level cache) so that every step reads its inputs from HBM. Before the
 warm-up steps the step runs untimed for --settle seconds (0.3 s), the time the GPU takes to reach
@@ -33,7 +39,8 @@ hipEventDisableSystemFence, so that recording them does not flush the caches bet
 they bracket); its `traffic` is the measured memory
 traffic per launch from the committed counter summary (headline workload only), reported only while
 the summary's kernel source hash matches the current source. `cpu_baseline` times the CPU oracle on
-a bounded sample of the same step.
+a bounded sample of the same step, at one thread and at every host thread the process may use (up
+to 16), and adds the CPU model and an fp32 torch.matmul on the host as a BLAS reference point.
 
 `--copy-calibration MIB` instead runs only a plain device-to-device copy of MIB MiB a few times
 (the reference kernel whose FETCH_SIZE / WRITE_SIZE counter readings calibrate the GEMM's).
@@ -95,12 +102,32 @@ WORKLOADS = {
 }
 
 
+# the two latency-bound workloads (under 1 MB each), reported in microseconds
+SMALL_WORKLOADS = {
+    "tiny_mxfp4": "A, B fp32 256x256 ~ N(0,1), A's largest entry x50: MXFP4 quantize of both (E8M0 "
+                  "floor, RNE, no rotation), the 256^3 MXFP4 GEMM (fp32 out), and A's per-tensor "
+                  "fp32-scale quantize (the outlier collapse)",
+    "mnist_mlp": "fp32 weights 256x784, 128x256, 10x128 ~ N(0, 0.05^2), clean and with fc1's largest "
+                 "entry x50: every {per-tensor, per-row, group-32 (flattened)} x {fp32 S = amax/6, E8M0 "
+                 "floor, E8M0 ceil} quantization to E2M1 (quantize only), with the MSE of each",
+}
+
+# The caveduck.io post's figures for the trained MNIST MLP (unstated machine): context only, the
+# synthetic weights here are random stand-ins with the same shapes.
+PAGE_MSE_CONTEXT = {
+    "table1_fc1_mse_clean_to_outlier": {"per_tensor": [5.4e-5, 1.2e-3], "per_channel": [1.7e-5, 2.3e-5],
+                                        "group32": [1.2e-5, 1.2e-5]},
+    "table2_group32_fp32_vs_pow2_mse": {"fc1": [1.23e-5, 1.58e-5], "fc2": [2.66e-5, 3.62e-5],
+                                        "fc3": [6.12e-5, 6.30e-5]},
+}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS) + sorted(SMALL_WORKLOADS))
     ap.add_argument("--copies", type=int, default=4, help="input copies cycled through (> LLC)")
     ap.add_argument("--settle", type=float, default=0.3,
                     help="seconds of untimed steps before the warm-up steps (clock ramp-up)")
@@ -233,10 +260,94 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
+def host_threads() -> int:
+    """Threads the CPU baseline may use: the host cores this process may run on, capped at the 16
+    that one GPU's share of a GPU host provides."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _slices(n, parts, align):
+    """[lo, hi) row ranges covering n rows in at most `parts` pieces, cut at multiples of align."""
+    step = max(align, -(-n // parts) // align * align)
+    return [(lo, min(n, lo + step)) for lo in range(0, n, step)]
+
+
+def _oracle_step(orc, As, Bs, pa, pb, K, threads, out_q=None, ga=None, gb=None):
+    """The oracle's pass over a sample: quantize A and B rows, their fp64 operand values, the fp64
+    GEMM of the sampled block (and its output quantize). With threads > 1 the rows are cut into
+    slices run on a thread pool (the C oracle releases the interpreter lock while it runs); the SR
+    element index and an NVFP4 tensor amax then restart per slice, the work is the same.
+    Returns (seconds for the quantize part, seconds for the GEMM part)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def q(x, p, ts=None):
+        return orc.quantize(x, elem=p.elem, block=p.block, scale_mode=p.scale_mode,
+                            round_mode=p.round_mode, hadamard_n=p.hadamard_n, seed=p.seed,
+                            tensor_scale=ts)
+
+    def operand(x, p, ts):
+        rows = x.shape[0]
+        c, s, t = q(x, p, ts)
+        if p.block[0] == 1:
+            return orc.operand_f64(c, s, t, rows, K, elem=p.elem, block=p.block, scale_mode=p.scale_mode)
+        srow = np.ascontiguousarray(s.reshape(rows // 32, -1)[np.arange(rows) // 32])  # 2D tiles
+        return orc.operand_f64(c, srow, t, rows, K, elem=p.elem, block=(1, 32), scale_mode=p.scale_mode)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        t0 = time.perf_counter()
+        fa = [ex.submit(operand, As[lo:hi], pa, ga) for lo, hi in _slices(As.shape[0], threads, 32)]
+        fb = [ex.submit(operand, Bs[lo:hi], pb, gb) for lo, hi in _slices(Bs.shape[0], threads, 32)]
+        a64 = np.concatenate([f.result() for f in fa])
+        b64 = np.concatenate([f.result() for f in fb])
+        t1 = time.perf_counter()
+
+        def gemm_rows(lo, hi):
+            c, _ = orc.gemm_f64(a64[lo:hi], b64)
+            if out_q is not None:
+                q(c.astype(np.float32), out_q)
+            return c
+
+        parts = [ex.submit(gemm_rows, lo, hi) for lo, hi in _slices(a64.shape[0], threads, 1)]
+        for f in parts:
+            f.result()
+        t2 = time.perf_counter()
+    return t1 - t0, t2 - t1
+
+
+def blas_reference(M, N, K):
+    """torch.matmul in fp32 on the host CPU for the same M x N x K (random operands), as a BLAS
+    reference point for the GEMM; TFLOP/s and the threads torch uses."""
+    import torch
+    g = torch.Generator().manual_seed(0)
+    a = torch.randn(M, K, generator=g)
+    b = torch.randn(N, K, generator=g)
+    torch.matmul(a[:64], b[:64].T)  # warm the library up
+    t0 = time.perf_counter()
+    torch.matmul(a, b.T)
+    dt = time.perf_counter() - t0
+    return {"TFLOP/s": round(2.0 * M * N * K / dt / 1e12, 4), "threads": torch.get_num_threads(),
+            "s": round(dt, 3), "what": f"torch.matmul fp32 on the host CPU, {M}x{N}x{K}"}
+
+
 def cpu_baseline(wk, a_bits, b_bits, pa, pb, f, out_q=None, ga=None, gb=None):
     """Time the oracle on f*M rows of A, f*N rows of B and the f*M x f*N block of C (and its output
-    quantize), and scale to a whole step: T = T_quantize / f + T_gemm / f^2. Column-wise operands
-    sample columns of the stored tensors (rows of their transposes)."""
+    quantize), at one thread and at all host threads, and scale each to a whole step:
+    T = T_quantize / f + T_gemm / f^2. Column-wise operands sample columns of the stored tensors
+    (rows of their transposes). Also reports the CPU model and a BLAS fp32 matmul reference."""
     import oracle as orc
     M, N, K = wk["M"], wk["N"], wk["K"]
     sm, sn = max(int(M * f) // 32 * 32, 32), max(int(N * f) // 32 * 32, 32)  # whole 32-row tiles
@@ -248,39 +359,196 @@ def cpu_baseline(wk, a_bits, b_bits, pa, pb, f, out_q=None, ga=None, gb=None):
     else:
         As = np.ascontiguousarray(a_bits[:sm])
         Bs = np.ascontiguousarray(b_bits[:sn])
-
-    def q(x, p, ts=None):
-        return orc.quantize(x, elem=p.elem, block=p.block, scale_mode=p.scale_mode,
-                            round_mode=p.round_mode, hadamard_n=p.hadamard_n, seed=p.seed,
-                            tensor_scale=ts)
-
-    t0 = time.perf_counter()
-    ca, sa, ta = q(As, pa, ga)
-    cb, sb, tb = q(Bs, pb, gb)
-    t1 = time.perf_counter()
-    a64 = orc.operand_f64(ca, sa, ta, sm, K, elem=pa.elem, block=pa.block, scale_mode=pa.scale_mode)
-    if pb.block[0] == 1:
-        b64 = orc.operand_f64(cb, sb, tb, sn, K, elem=pb.elem, block=pb.block, scale_mode=pb.scale_mode)
-    else:  # 2D tiles: each row takes its tile row's scales
-        srow = np.ascontiguousarray(sb.reshape(sn // 32, -1)[np.arange(sn) // 32])
-        b64 = orc.operand_f64(cb, srow, tb, sn, K, elem=pb.elem, block=(1, 32), scale_mode=pb.scale_mode)
-    c64, _ = orc.gemm_f64(a64, b64)
-    if out_q is not None:
-        q(c64.astype(np.float32), out_q)
-    t2 = time.perf_counter()
     fm, fn = sm / M, sn / N
-    t_step = (t1 - t0) / ((fm + fn) / 2) + (t2 - t1) / (fm * fn)
+    flops = 2.0 * M * N * K
+    runs = {}
+    nthreads = host_threads()
+    for th in sorted({1, nthreads}):
+        tq, tg = _oracle_step(orc, As, Bs, pa, pb, K, th, out_q=out_q, ga=ga, gb=gb)
+        t_step = tq / ((fm + fn) / 2) + tg / (fm * fn)
+        runs[th] = dict(value=round(flops / t_step / 1e12, 6), step_s=round(t_step, 3),
+                        tq=round(tq, 2), tg=round(tg, 2))
+    best = runs[nthreads]
     return {
-        "value": round(2.0 * M * N * K / t_step / 1e12, 6),
+        "value": best["value"],
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": nthreads,
         "kind": "oracle",
-        "sample": (f"oracle quantize of {sm} A rows + {sn} B rows ({t1 - t0:.2f} s) and the fp64 "
-                   f"GEMM of their {sm}x{sn} block over K={K}"
-                   f"{' with its output quantize' if out_q is not None else ''} ({t2 - t1:.2f} s), "
-                   f"scaled to a full step as T_q/f + T_gemm/f^2 with f={f} (the sampled row fractions)"),
-        "step_s": round(t_step, 3),
+        "sample": (f"oracle quantize of {sm} A rows + {sn} B rows and the fp64 GEMM of their {sm}x{sn} "
+                   f"block over K={K}{' with its output quantize' if out_q is not None else ''}, scaled to a "
+                   f"full step as T_q/f + T_gemm/f^2 with f={f}; at {nthreads} threads: {best['tq']} s + "
+                   f"{best['tg']} s (row slices on a thread pool), at 1 thread: {runs[1]['tq']} s + {runs[1]['tg']} s"),
+        "step_s": best["step_s"],
+        "single_thread": {"value": runs[1]["value"], "step_s": runs[1]["step_s"], "cores": 1},
+        "cpu_model": cpu_model(),
+        "blas_fp32": blas_reference(M, N, K),
     }
+
+
+def _timed_steps(step, args, nparts):
+    """Run step(i, ev) untimed for --settle seconds and --warmup steps, then time --steps steps with
+    fence-free HIP events (ev[(nparts + 1) * i + j] before part j of step i, one after the last).
+    Returns (wall seconds per step, mean seconds of each part)."""
+    import torch
+    t_settle = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(20):
+            step(i, None)
+            i += 1
+        torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    per = nparts + 1
+    evs = [HipTimingEvent(stream) for _ in range(per * args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[per * i:per * i + per])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    parts = [float(np.mean([evs[per * i + j].elapsed_time(evs[per * i + j + 1]) for i in range(args.steps)])) * 1e-3
+             for j in range(nparts)]
+    return wall, parts
+
+
+def _base_line(args, value, unit, dtype, config, wall):
+    return {"metric": "quantize GB/s (% HBM peak); MXFP4 GEMM TFLOP/s (% FP4 MFMA peak)", "value": value,
+            "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(wall * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic (seeded numpy draws of the workload's shapes and distributions)", "config": config}
+
+
+def run_tiny(args):
+    """Tiny MXFP4 check: quantize A and B (MXFP4), the 256^3 GEMM, and A's per-tensor quantize."""
+    import torch
+    import oracle as orc
+    from bit_gemm_fwht_amd import fp4
+    from bit_gemm_fwht_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    a, b = wl.tiny_mxfp4(0)
+    at = torch.from_numpy(a).to(dev)
+    bt = torch.from_numpy(b).to(dev)
+    mx = fp4.Params()
+    pt = fp4.Params(block=(256, 256), scale_mode=fp4.SCALE_F32)
+    qa, qb, qt = (fp4.empty_qtensor(256, 256, p, dev) for p in (mx, mx, pt))
+    ws = torch.empty(fp4.buffer_sizes(256, 256, pt)[2], dtype=torch.uint8, device=dev)
+    c = torch.empty(256, 256, dtype=torch.float32, device=dev)
+
+    def step(i, ev):
+        if ev: ev[0].record()
+        fp4.quantize(at, mx, out=qa)
+        fp4.quantize(bt, mx, out=qb)
+        if ev: ev[1].record()
+        fp4.gemm(qa, qb, out=c)
+        if ev: ev[2].record()
+        fp4.quantize(at, pt, out=qt, workspace=ws)
+        if ev: ev[3].record()
+
+    wall, (tq, tg, tt) = _timed_steps(step, args, 3)
+    flops = 2.0 * 256**3
+    qbytes = 2 * (256 * 256 * 4 + 256 * 128 + 256 * 8) + 256 * 256 * 4 + 256 * 128 + 4
+    codes = qt.codes.cpu().numpy()
+    nonzero = int(np.count_nonzero(codes & 0x7) + np.count_nonzero((codes >> 4) & 0x7))
+    # the oracle over the same step (it is small enough to run whole)
+    t0 = time.perf_counter()
+    ca, sa, _ = orc.quantize(a)
+    cb, sb, _ = orc.quantize(b)
+    c64, _ = orc.gemm_f64(orc.operand_f64(ca, sa, None, 256, 256), orc.operand_f64(cb, sb, None, 256, 256))
+    orc.quantize(a, block=(256, 256), scale_mode=orc.SCALE_F32)
+    t_orc = time.perf_counter() - t0
+    err = float(np.abs(c.cpu().numpy().astype(np.float64) - c64).max())
+    out = _base_line(args, round(flops / wall / 1e12, 4), "TFLOP/s", "mxfp4",
+                     {"workload": "tiny_mxfp4", "M": 256, "N": 256, "K": 256, "input": "fp32",
+                      "quant": "E2M1 + E8M0 per 32 (floor), RNE; A also per tensor with fp32 S = amax/6",
+                      "output": "fp32"}, wall)
+    out.update({
+        "latency_us": {"step": round(wall * 1e6, 2), "quantize_a_b": round(tq * 1e6, 2), "gemm": round(tg * 1e6, 2),
+                       "per_tensor_quantize_a": round(tt * 1e6, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(flops / tg / 1e12, 3), "peak": FP4_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flops / tg / 1e12 / FP4_PEAK_TFLOPS, 6), "traffic": None,
+                     "note": "33.6 MFLOP on 256 x 256 outputs: one 256x256 tile, launch-latency bound"},
+        "quantize": {"GB/s": round(qbytes / (tq + tt) / 1e9, 2), "frac": round(qbytes / (tq + tt) / 1e9 / HBM_PEAK_GBS, 6),
+                     "us": round((tq + tt) * 1e6, 2), "bytes": qbytes},
+        "checks": {"per_tensor_nonzero_codes": nonzero, "gemm_max_abs_err_vs_fp64_oracle": err},
+        "cpu_baseline": {"value": round(flops / t_orc / 1e12, 8), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                         "sample": f"the whole step on the oracle: {t_orc * 1e3:.1f} ms", "cpu_model": cpu_model()},
+    })
+    print(json.dumps(out), flush=True)
+
+
+def run_mnist(args):
+    """MNIST-MLP-shaped weight quantization: every granularity x scale variant, clean and with the
+    50x outlier in fc1, quantize-only; the MSE of each from the GPU's dequantized values (identical to
+    the oracle's, which is checked)."""
+    import torch
+    import oracle as orc
+    from bit_gemm_fwht_amd import fp4
+    from bit_gemm_fwht_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    sets = {"clean": wl.mnist_mlp(0, outlier=False), "outlier": wl.mnist_mlp(0, outlier=True)}
+    scales = {"fp32": fp4.SCALE_F32, "e8m0_floor": fp4.SCALE_E8M0_FLOOR, "e8m0_ceil": fp4.SCALE_E8M0_CEIL}
+    jobs = []  # (set, layer, granularity, scale, host array as quantized, device tensor, params, qtensor, ws)
+    for sname, layers in sets.items():
+        for lname, w in layers.items():
+            for gran in ("per_tensor", "per_row", "group32"):
+                x = w.reshape(1, -1) if gran == "group32" else w
+                rows, cols = x.shape
+                block = {"per_tensor": (rows, cols), "per_row": (1, cols), "group32": (1, 32)}[gran]
+                xt = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+                for scn, sm in scales.items():
+                    p = fp4.Params(block=block, scale_mode=sm)
+                    q = fp4.empty_qtensor(rows, cols, p, dev)
+                    wb = fp4.buffer_sizes(rows, cols, p)[2]
+                    ws = torch.empty(wb, dtype=torch.uint8, device=dev) if wb else None
+                    jobs.append((sname, lname, gran, scn, np.ascontiguousarray(x), xt, p, q, ws))
+
+    def step(i, ev):
+        if ev: ev[0].record()
+        for j in jobs:
+            fp4.quantize(j[5], j[6], out=j[7], workspace=j[8])
+        if ev: ev[1].record()
+
+    wall, (tq,) = _timed_steps(step, args, 1)
+    nbytes = 0
+    mse = {}
+    t_orc = 0.0
+    outlier_at = np.unravel_index(int(np.argmax(np.abs(sets["outlier"]["fc1"]))), sets["outlier"]["fc1"].shape)
+    for sname, lname, gran, scn, x, xt, p, q, ws in jobs:
+        cb, sb, _ = fp4.buffer_sizes(x.shape[0], x.shape[1], p)
+        nbytes += x.size * 4 + cb + sb
+        y = fp4.dequantize(q).cpu().numpy().astype(np.float64)
+        d2 = (y - x.astype(np.float64)) ** 2
+        t0 = time.perf_counter()
+        oc, os_, _ = orc.quantize(x, block=p.block, scale_mode=p.scale_mode)
+        yo = orc.dequantize(oc, os_, None, x.shape[0], x.shape[1], block=p.block, scale_mode=p.scale_mode)
+        t_orc += time.perf_counter() - t0
+        entry = {"mse": float(d2.mean()), "oracle_equal": bool(np.array_equal(y, yo.astype(np.float64)))}
+        if sname == "outlier" and lname == "fc1":
+            keep = np.ones(sets["outlier"]["fc1"].shape, dtype=bool)
+            keep[outlier_at] = False
+            entry["mse_without_outlier"] = float(d2.reshape(keep.shape)[keep].mean())
+        mse.setdefault(sname, {}).setdefault(lname, {}).setdefault(gran, {})[scn] = entry
+    out = _base_line(args, round(nbytes / tq / 1e9, 3), "GB/s", "e2m1",
+                     {"workload": "mnist_mlp", "tensors": "fc1 256x784, fc2 128x256, fc3 10x128 fp32",
+                      "variants": len(jobs), "input": "fp32", "quant": "E2M1; per tensor / per row / per 32 (flattened); "
+                      "fp32 S = amax/6, E8M0 floor, E8M0 ceil; RNE"}, wall)
+    out.update({
+        "latency_us": {"step": round(wall * 1e6, 2), "quantize_all_variants": round(tq * 1e6, 2),
+                       "launches": len(jobs)},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / tq / 1e9, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / tq / 1e9 / HBM_PEAK_GBS, 6), "traffic": None,
+                     "note": f"{len(jobs)} launches over 0.94 MB of weights: launch-latency bound"},
+        "mse": mse,
+        "page_context": PAGE_MSE_CONTEXT,
+        "cpu_baseline": {"value": round(nbytes / t_orc / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                         "sample": f"every variant quantized and dequantized on the oracle: {t_orc * 1e3:.1f} ms",
+                         "cpu_model": cpu_model()},
+    })
+    print(json.dumps(out), flush=True)
 
 
 def main():
@@ -297,6 +565,10 @@ def main():
     from bit_gemm_fwht_amd import fp4
 
     fp4.lib()  # fail loudly if the HIP library is missing
+    if args.workload == "tiny_mxfp4":
+        return run_tiny(args)
+    if args.workload == "mnist_mlp":
+        return run_mnist(args)
     dev = torch.device("cuda:0")
     wk = WORKLOADS[args.workload]
     M, N, K = wk["M"], wk["N"], wk["K"]

@@ -120,3 +120,21 @@ def test_given_scale_is_the_tensors_own_nvfp4_scale():
     c1, s1, _ = orc.quantize(x, block=(1, 16), scale_mode=orc.SCALE_NV_4OVER6)
     c2, s2, _ = orc.quantize(x, block=(1, 16), scale_mode=orc.SCALE_NV_4OVER6_GIVEN, tensor_scale=g)
     assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+def test_cpu_baseline_slices_cover_the_rows():
+    for n, parts, align in ((1536, 16, 32), (4128, 8, 32), (64, 16, 32), (1, 4, 1), (1000, 3, 1)):
+        s = bench._slices(n, parts, align)
+        assert s[0][0] == 0 and s[-1][1] == n and len(s) <= parts
+        assert all(a[1] == b[0] for a, b in zip(s, s[1:]))
+        assert all(lo % align == 0 for lo, _ in s)
+    assert 1 <= bench.host_threads() <= 16
+    assert isinstance(bench.cpu_model(), str)
+
+
+def test_small_workloads_are_selectable():
+    assert set(bench.SMALL_WORKLOADS) == {"tiny_mxfp4", "mnist_mlp"}
+    for name in bench.SMALL_WORKLOADS:
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2", "--workload", name],
+                           capture_output=True, text=True, timeout=120)
+        assert r.returncode == 2 and "one GPU" in r.stderr  # parsed, then refused before any GPU work
