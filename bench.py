@@ -282,7 +282,7 @@ def cpu_model() -> str:
 
 def _slices(n, parts, align):
     """[lo, hi) row ranges covering n rows in at most `parts` pieces, cut at multiples of align."""
-    step = max(align, -(-n // parts) // align * align)
+    step = -(-(-(-n // parts)) // align) * align  # ceil(ceil(n / parts) / align) * align
     return [(lo, min(n, lo + step)) for lo in range(0, n, step)]
 
 
