@@ -17,6 +17,9 @@ and three that measure extensions of the path:
                      taken once before timing): one quantize pass per tensor, no amax pass
   llama7b_fused_out_q the headline with the fused output quantize: C (bf16) and C_q (MXFP4,
                      H_128 along N, E8M0 floor, RNE) from the GEMM's epilogue
+  forward_2d_transposed Y = X W at the backward's shapes (8192 x 4096 x 4096): W [K, N] quantized once
+                     with 2D 32x32 truncation-free scales as stored, re-laid out each step as the
+                     quantized W^T the GEMM takes (no re-quantization), X group-32 truncation-free
   backward_dw_colwise dW = dY^T X over 8192 tokens (4096 x 4096 x 8192): dY and X as stored
                      [tokens, features], quantized column-wise (along tokens, H_128, E8M0 ceil;
                      dY with Philox SR) without forming the transposes
@@ -94,6 +97,12 @@ WORKLOADS = {
         out_q=dict(hadamard_n=128),
         quant="E2M1 + E8M0 per 32 (floor), RNE; C_q: the same along N after H_128", fp8=False, f=0.375,
         kernel="k_gemm_big (MXFP4, bf16 C + fused H_128 MXFP4 quantize of C along N)"),
+    "forward_2d_transposed": dict(
+        M=8192, N=4096, K=4096, a=dict(scale="ceil"), b=dict(block=(32, 32), scale="ceil"), batched=False,
+        transposed_b=True,
+        quant="X: E2M1 + E8M0 per 32 (ceil), RNE; W: E2M1 + E8M0 per 32x32 (ceil), RNE, quantized once as "
+              "stored [K, N] and re-laid out as its transpose each step",
+        fp8=False, f=0.375, kernel="k_gemm_big (MXFP4, 2D B scales from the transposed weight, bf16 out)"),
     "backward_dw_colwise": dict(
         M=4096, N=4096, K=8192, a=dict(hadamard_n=128, scale="ceil", sr=True),
         b=dict(hadamard_n=128, scale="ceil"), batched=False, colwise=True,
@@ -164,6 +173,8 @@ def inputs_of(name):
         return x, w
     if name == "backward_dw_colwise":
         return wl.backward_dw(0)  # dY [tokens, 4096], X [tokens, 4096]
+    if name == "forward_2d_transposed":
+        return wl.forward_2d(0)  # X [8192, 4096], W [4096 (K), 4096 (N)]
     return wl.nvfp4_4over6(0)
 
 
@@ -355,6 +366,9 @@ def cpu_baseline(wk, a_bits, b_bits, pa, pb, f, out_q=None, ga=None, gb=None):
         sn = max(sn // out_q.hadamard_n * out_q.hadamard_n, out_q.hadamard_n)
     if wk.get("colwise"):
         As = np.ascontiguousarray(a_bits[:, :sm].T)
+        Bs = np.ascontiguousarray(b_bits[:, :sn].T)
+    elif wk.get("transposed_b"):  # the oracle quantizes W^T's rows directly
+        As = np.ascontiguousarray(a_bits[:sm])
         Bs = np.ascontiguousarray(b_bits[:, :sn].T)
     else:
         As = np.ascontiguousarray(a_bits[:sm])
@@ -581,6 +595,10 @@ def main():
     qa = [fp4.empty_qtensor(M, K, pa, dev) for _ in range(args.copies)]
     qb = [fp4.empty_qtensor(N, K, pb, dev) for _ in range(args.copies)]
     cs = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(args.copies)]
+    transposed_b = bool(wk.get("transposed_b"))
+    if transposed_b:  # W [K, N] quantized once as stored (2D tiles); each step re-lays it out as W^T
+        qw_stored = [fp4.quantize(Bs[j], pb) for j in range(args.copies)]
+        torch.cuda.synchronize()
     colwise = bool(wk.get("colwise"))
     quantize_one = fp4.quantize_colwise if colwise else fp4.quantize
     # delayed tensor scales: g of each tensor from its own amax, set once in the outputs' buffers
@@ -616,6 +634,9 @@ def main():
             ev[2 * i].record()
         if wk["batched"]:
             fp4.quantize_batch([As[j], Bs[j]], pa, outs=[qa[j], qb[j]])
+        elif transposed_b:
+            fp4.transpose_2d(qw_stored[j], out=qb[j])
+            quantize_one(As[j], pa, out=qa[j], workspace=wsa)
         else:
             quantize_one(As[j], pa, out=qa[j], workspace=wsa,
                          tensor_scale=qa[j].tensor_scale if ga is not None else None)
@@ -661,6 +682,9 @@ def main():
         return rows * K * 2 + cb + sb
 
     bytes_q = qbytes(M, pa) + qbytes(N, pb)
+    if transposed_b:  # the re-layout reads and writes W's codes and scales once
+        cbw, sbw, _ = fp4.buffer_sizes(N, K, pb)
+        bytes_q = qbytes(M, pa) + 2 * (cbw + sbw)
     gemm_tflops = flops / t_g / 1e12
     peak = FP8_PEAK_TFLOPS if wk["fp8"] else FP4_PEAK_TFLOPS
     dtype = "nvfp4" if args.workload.startswith("nvfp4") else {False: "mxfp4", True: "mxfp8"}[wk["fp8"]]
@@ -688,6 +712,7 @@ def main():
                      "frac": round(bytes_q / tq / 1e9 / HBM_PEAK_GBS, 4),
                      "us": round(tq * 1e6, 2), "bytes": int(bytes_q),
                      "launches": ("one batched k_segment launch for A and B" if wk["batched"]
+                                  else "quantize of A + the 2D re-layout of B's codes" if transposed_b
                                   else "separate launches for A and B")
                      + (", column-wise" if colwise else "") + (", given tensor scales" if ga is not None else "")},
         "gemm": {"TFLOP/s": round(gemm_tflops, 2), "frac": round(gemm_tflops / peak, 4),

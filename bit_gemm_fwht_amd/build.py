@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbgf.so")
-SOURCES = ["fp4_abi.cpp", "quantize.hip", "gemm.hip"]
+SOURCES = ["fp4_abi.cpp", "quantize.hip", "gemm.hip", "transpose.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -528,6 +528,33 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
     }
 }
 
+int fp4_transpose_2d(const void* codes, const void* scales, int64_t rows, int64_t cols, const fp4_qparams* p,
+                     void* out_codes, void* out_scales, void* stream) {
+    try {
+        Layout lay;
+        int rc = check_params(rows, cols, p, &lay);
+        if (rc != FP4_OK) return rc;
+        if (lay != L_SEG2D || p->hadamard_n != 0) return FP4_ERR_UNSUPPORTED;
+        if (!codes || !scales || !out_codes || !out_scales) return FP4_ERR_INVALID_ARG;
+        const void* ins[2] = {codes, scales};
+        for (const void* q : ins)
+            if (q == out_codes || q == out_scales) return FP4_ERR_INVALID_ARG;
+        if (out_codes == out_scales) return FP4_ERR_INVALID_ARG;
+        if (!aligned(codes, 16) || !aligned(out_codes, 16)) return FP4_ERR_ALIGNMENT;
+        TransposeArgs t{};
+        t.codes = reinterpret_cast<const uint8_t*>(codes);
+        t.scales = reinterpret_cast<const uint8_t*>(scales);
+        t.rows = rows;
+        t.cols = cols;
+        t.out_codes = reinterpret_cast<uint8_t*>(out_codes);
+        t.out_scales = reinterpret_cast<uint8_t*>(out_scales);
+        return hip_status(launch_transpose_2d(t, p->elem == FP4_ELEM_E2M1 ? ELEM_E2M1 : ELEM_E4M3,
+                                              reinterpret_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return FP4_ERR_INTERNAL;
+    }
+}
+
 int fp4_nvfp4_to_mxfp8(const void* codes, const void* scales, int64_t rows, int64_t cols, void* out_codes,
                        void* out_scales, void* stream) {
     try {

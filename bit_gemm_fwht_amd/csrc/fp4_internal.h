@@ -72,6 +72,16 @@ hipError_t launch_dequant_segment(const DeqArgs& a, int elem, int sc, int br, in
                                   int out_dtype, hipStream_t s);
 hipError_t launch_dequant_rowblock(const DeqArgs& a, int elem, int sc, int out_dtype, hipStream_t s);
 
+// 2D (32 x 32) quantized tensor [rows, cols] -> the quantized form of its transpose [cols, rows]
+struct TransposeArgs {
+    const uint8_t* codes;
+    const uint8_t* scales;
+    int64_t rows, cols;
+    uint8_t* out_codes;
+    uint8_t* out_scales;
+};
+hipError_t launch_transpose_2d(const TransposeArgs& a, int elem, hipStream_t s);
+
 // GEMM
 struct GemmArgs {
     const uint8_t* a;        // [M, K/2] (E2M1) or [M, K] (E4M3)

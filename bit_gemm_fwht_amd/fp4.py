@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
     L.fp4_gemm.restype = ctypes.c_int
     L.fp4_quantize_noalloc.argtypes = [P, I32, I64, I64, I64, QP, P, P, P, P]
     L.fp4_quantize_noalloc.restype = ctypes.c_int
+    L.fp4_transpose_2d.argtypes = [P, P, I64, I64, QP, P, P, P]
+    L.fp4_transpose_2d.restype = ctypes.c_int
     L.fp4_nvfp4_to_mxfp8.argtypes = [P, P, I64, I64, P, P, P]
     L.fp4_nvfp4_to_mxfp8.restype = ctypes.c_int
     _lib = L
@@ -403,6 +405,22 @@ def gemm(a: QTensor, b: QTensor, out_dtype=torch.bfloat16, out: torch.Tensor | N
         q_out.rows, q_out.cols, q_out.params, q_out.tensor_scale = a.rows, b.rows, out_q, None
         return c, q_out
     return c
+
+
+def transpose_2d(q: QTensor, out: QTensor | None = None) -> QTensor:
+    """The quantized transpose [cols, rows] of a tensor quantized with 32 x 32 blocks (a re-layout:
+    the same codes and scales fp4_quantize gives the transposed tensor)."""
+    dev = q.codes.device
+    _check_q(q, q.rows, q.cols, q.params, dev, "q")
+    if out is not None:
+        _check_q(out, q.cols, q.rows, q.params, dev, "out")
+    t = out if out is not None else empty_qtensor(q.cols, q.rows, q.params, dev)
+    p = q.params.c()
+    st = lib().fp4_transpose_2d(q.codes.data_ptr(), q.scales.data_ptr(), q.rows, q.cols, ctypes.byref(p),
+                                t.codes.data_ptr(), t.scales.data_ptr(), _stream_ptr(dev))
+    _check(st, "fp4_transpose_2d")
+    t.rows, t.cols, t.params = q.cols, q.rows, q.params
+    return t
 
 
 def nvfp4_to_mxfp8(q: QTensor) -> QTensor:

@@ -15,6 +15,8 @@ used trained weights or datasets that are not available here):
   backward_2d   W bf16 4096x4096 ~ N(0, 0.02^2); dY bf16 8192x4096 ~ Student-t(3) x 1e-3.
   nvfp4_4over6  X bf16 8192x8192 ~ Laplace(0,1) with 0.1% of entries x30; W bf16 8192x8192
                 ~ N(0, 0.02^2).
+  forward_2d    X bf16 8192x4096 ~ Student-t(3), W bf16 4096x4096 ~ N(0, 0.02^2): Y = X W with W
+                contracted along its first axis (the 2D-quantized weight reused through its transpose).
   backward_dw   dY bf16 8192x4096 ~ Student-t(3) x 1e-3 and X bf16 8192x4096 ~ N(0,1) with 1% of
                 channels x20: the operands of dW = dY^T X (the column-wise quantize).
 Every generator takes its own numpy Generator seeded with `seed`, and draws the tensors in the
@@ -83,6 +85,16 @@ def backward_2d(seed: int = 0, m: int = 8192, n: int = 4096, k: int = 4096):
     w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
     dy = (rng.standard_t(3.0, size=(m, k)) * 1e-3).astype(np.float32)
     return f32_to_bf16_bits(w), f32_to_bf16_bits(dy)
+
+
+def forward_2d(seed: int = 0, m: int = 8192, k: int = 4096, n: int = 4096):
+    """X [m, k] ~ Student-t(3) (activations) and W [k, n] ~ N(0, 0.02^2) as bf16 bits: the forward
+    Y = X W of the layer whose weight the backward workload quantizes with 2D blocks, contracting W
+    along its first (non-contiguous) axis."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_t(3.0, size=(m, k)).astype(np.float32)
+    w = rng.standard_normal((k, n), dtype=np.float32) * np.float32(0.02)
+    return f32_to_bf16_bits(x), f32_to_bf16_bits(w)
 
 
 def nvfp4_4over6(seed: int = 0, m: int = 8192, n: int = 8192, k: int = 8192):

@@ -226,6 +226,20 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
              const fp4_qparams* out_q, fp4_qtensor* C_q, void* workspace, int64_t ws_bytes,
              void* stream);
 
+/* The quantized form of the transpose of a tensor quantized with 32 x 32 blocks ((32, 32) E8M0 tiles,
+ * E2M1 or E4M3 elements, hadamard_n == 0): codes / scales of T [rows, cols] become out_codes /
+ * out_scales of T^T [cols, rows], exactly what fp4_quantize with the same *p returns for T^T (one
+ * scale per 32 x 32 tile makes each tile of T^T the same elements, amax and scale as a tile of T:
+ * "Stable FP4 Training via Transposition-Invariant Block Quantization", abstract), so a weight
+ * quantized once serves GEMMs that contract it along either axis. A pure re-layout (no arithmetic):
+ * element (r, c) moves to (c, r) and scale (i, j) to (j, i). With a rotation the codes describe the
+ * rotated tensor, whose transpose is rotated along the other axis, so hadamard_n != 0 returns
+ * FP4_ERR_UNSUPPORTED. Layouts as everywhere: out_codes [cols, rows/2] (E2M1) or [cols, rows]
+ * (E4M3), out_scales [cols/32, rows/32]; codes and out_codes 16-byte aligned (else
+ * FP4_ERR_ALIGNMENT); outputs must not alias the inputs. */
+int fp4_transpose_2d(const void* codes, const void* scales, int64_t rows, int64_t cols, const fp4_qparams* p,
+                     void* out_codes, void* out_scales, void* stream);
+
 /* The FP8 re-expression of an NVFP4 tensor, the operand form the GEMM multiplies NVFP4 x NVFP4 in
  * (the gfx950 scaled matrix instructions take one power-of-two scale per 32 K values): codes
  * (E2M1 [rows, cols/2]) and scales (E4M3 [rows, cols/16], the (1, 16) blocks of the NVFP4 modes of

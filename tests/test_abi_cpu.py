@@ -295,3 +295,22 @@ def test_nvfp4_to_mxfp8_rejects_bad_arguments(fp4):
     assert call(oc=0x30004) == E.ERR_ALIGNMENT
     assert call(oc=0x10000) == E.ERR_INVALID_ARG      # output aliases an input
     assert call(os=0x30000) == E.ERR_INVALID_ARG      # outputs alias each other
+
+
+def test_transpose_2d_rejects_bad_arguments(fp4):
+    L = fp4.lib()
+    p2d = P(fp4, block_rows=32, block_cols=32, scale_mode=1)
+    g = dict(codes=0x10000, scales=0x20000, rows=64, cols=96, oc=0x30000, os=0x40000, p=p2d)
+
+    def call(**kw):
+        a = dict(g, **kw)
+        return L.fp4_transpose_2d(a["codes"], a["scales"], a["rows"], a["cols"], ctypes.byref(a["p"]), a["oc"],
+                                  a["os"], None)
+
+    assert call(p=P(fp4)) == fp4.ERR_UNSUPPORTED                          # 1 x 32 groups: not a 2D tensor
+    assert call(p=P(fp4, block_rows=32, scale_mode=1, hadamard_n=32)) == fp4.ERR_UNSUPPORTED  # rotated
+    assert call(rows=48) == fp4.ERR_INVALID_ARG                          # rows % 32
+    assert call(codes=None) == fp4.ERR_INVALID_ARG
+    assert call(oc=0x10000) == fp4.ERR_INVALID_ARG                       # aliases the input
+    assert call(codes=0x10008) == fp4.ERR_ALIGNMENT
+    assert call(oc=0x30008) == fp4.ERR_ALIGNMENT

@@ -38,7 +38,7 @@ def test_more_than_one_gpu_is_refused():
 @pytest.mark.parametrize("name", sorted(bench.WORKLOADS))
 def test_workload_quantization_is_valid(fp4, name):
     wk = bench.WORKLOADS[name]
-    for side, rows in (("a", wk["M"]), ("b", wk["N"])):
+    for side, rows in (("a", wk["M"]), ("b", wk["N"])):  # B as the GEMM takes it ([N, K])
         p = bench.params_of(fp4, wk[side])
         codes, scales, _ = fp4.buffer_sizes(rows, wk["K"], p)
         per = 1 if p.elem == fp4.E4M3 else 0.5
