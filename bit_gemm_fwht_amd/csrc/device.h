@@ -22,15 +22,9 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// round-to-nearest-even fp32 -> bf16 bits (inputs are finite)
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // Two fp32 values to packed bf16 (a in the low half), round to nearest even, with the hardware
-// convert (v_cvt_pk_bf16_f32); equal to bf16_rne_bits on every non-NaN input (checked exhaustively
-// on gfx950).
+// convert (v_cvt_pk_bf16_f32). Every bf16 output of the library (GEMM epilogues, dequantize) goes
+// through it; a GPU test sweeps it over every fp32 bit pattern.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
     typedef float f32x2_t __attribute__((ext_vector_type(2)));

@@ -245,14 +245,14 @@ __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
                 }
             } else {
                 uint16_t* cp = reinterpret_cast<uint16_t*>(g.c) + m * g.ldc + n;
-                const uint32_t w0 = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
-                const uint32_t w1 = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+                const uint32_t w0 = pack_bf16x2_rne(v[0], v[1]);
+                const uint32_t w1 = pack_bf16x2_rne(v[2], v[3]);
                 if (n + 3 < g.N && ((g.ldc & 3) == 0)) {
                     *reinterpret_cast<u32x2*>(cp) = (u32x2){w0, w1};
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (n + i < g.N) cp[i] = (uint16_t)bf16_rne_bits(v[i]);
+                        if (n + i < g.N) cp[i] = (uint16_t)pack_bf16x2_rne(v[i], 0.0f);
                 }
             }
         }

@@ -636,13 +636,13 @@ __global__ __launch_bounds__(kThreads) void k_dequant_segment(DeqArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
     } else {
+        // the hardware packed convert (round to nearest even), the one the GEMM epilogue uses
         uint4* y = reinterpret_cast<uint4*>(base);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             uint32_t w[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                w[j] = bf16_rne_bits(v[8 * i + 2 * j]) | (bf16_rne_bits(v[8 * i + 2 * j + 1]) << 16);
+            for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2_rne(v[8 * i + 2 * j], v[8 * i + 2 * j + 1]);
             y[i] = make_uint4(w[0], w[1], w[2], w[3]);
         }
     }
@@ -667,7 +667,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_rowblock(DeqArgs a) {
         }
         const float y = q * d;
         if constexpr (OUT == DT_F32) reinterpret_cast<float*>(a.y)[row * a.ldy + c] = y;
-        else reinterpret_cast<uint16_t*>(a.y)[row * a.ldy + c] = (uint16_t)bf16_rne_bits(y);
+        else reinterpret_cast<uint16_t*>(a.y)[row * a.ldy + c] = (uint16_t)pack_bf16x2_rne(y, 0.0f);
     }
 }
 
