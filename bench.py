@@ -12,6 +12,8 @@ forward linear:
   backward_2d_mxfp8  the same with E4M3 elements (MXFP8, the FP8 matrix cores)
   nvfp4_4over6       8192^3: X Laplace with 0.1% x30 outliers, W N(0, 0.02^2), NVFP4 with the
                      4/6 choice (tensor amax pass + quantize), GEMM through the FP8 re-expression
+  nvfp4_4over6_lds   the same with the FP8 re-expression done in LDS inside the GEMM (no pre-pass,
+                     no workspace)
 and three that measure extensions of the path:
   nvfp4_4over6_given the same with delayed tensor scales (g given, from each tensor's own amax
                      taken once before timing): one quantize pass per tensor, no amax pass
@@ -20,6 +22,9 @@ and three that measure extensions of the path:
   forward_2d_transposed Y = X W at the backward's shapes (8192 x 4096 x 4096): W [K, N] quantized once
                      with 2D 32x32 truncation-free scales as stored, re-laid out each step as the
                      quantized W^T the GEMM takes (no re-quantization), X group-32 truncation-free
+  llama7b_fused_quantize_a the headline with X's rotation + quantize fused into the GEMM launch (one
+                     persistent launch: the grid quantizes X, each tile waits for its rows); W keeps
+                     its own quantize launch; `gemm` then times X's quantize and the product together
   backward_dw_colwise dW = dY^T X over 8192 tokens (4096 x 4096 x 8192): dY and X as stored
                      [tokens, features], quantized column-wise (along tokens, H_128, E8M0 ceil;
                      dY with Philox SR) without forming the transposes
@@ -88,6 +93,10 @@ WORKLOADS = {
         M=8192, N=8192, K=8192, a=dict(nv46=True), b=dict(nv46=True), batched=False,
         quant="E2M1 + E4M3 per 16 x fp32 tensor scale, 4/6 choice, RNE", fp8=True, f=0.1875,
         kernel="fp4_gemm call: NVFP4->FP8 re-expression of both operands + k_gemm_big (FP8, bf16 out)"),
+    "nvfp4_4over6_lds": dict(
+        M=8192, N=8192, K=8192, a=dict(nv46=True), b=dict(nv46=True), batched=False, nv_lds=True,
+        quant="E2M1 + E4M3 per 16 x fp32 tensor scale, 4/6 choice, RNE", fp8=True, f=0.1875,
+        kernel="k_gemm_nv (NVFP4 operands re-expressed as FP8 in LDS, FP8 scaled MFMA, bf16 out; no workspace)"),
     "nvfp4_4over6_given": dict(
         M=8192, N=8192, K=8192, a=dict(nv46=True, given=True), b=dict(nv46=True, given=True), batched=False,
         quant="E2M1 + E4M3 per 16 x given fp32 tensor scale, 4/6 choice, RNE", fp8=True, f=0.1875,
@@ -103,6 +112,11 @@ WORKLOADS = {
         quant="X: E2M1 + E8M0 per 32 (ceil), RNE; W: E2M1 + E8M0 per 32x32 (ceil), RNE, quantized once as "
               "stored [K, N] and re-laid out as its transpose each step",
         fp8=False, f=0.375, kernel="k_gemm_big (MXFP4, 2D B scales from the transposed weight, bf16 out)"),
+    "llama7b_fused_quantize_a": dict(
+        M=4096, N=11008, K=4096, a=dict(hadamard_n=128), b=dict(hadamard_n=128), batched=False,
+        fused_a=True,
+        quant="E2M1 + E8M0 per 32 (floor), RNE; X rotated and quantized inside the GEMM launch", fp8=False,
+        f=0.375, kernel="k_gemm_fused_a (X's H_128 + MXFP4 quantize, then the 256x256 MXFP4 tiles, bf16 out)"),
     "backward_dw_colwise": dict(
         M=4096, N=4096, K=8192, a=dict(hadamard_n=128, scale="ceil", sr=True),
         b=dict(hadamard_n=128, scale="ceil"), batched=False, colwise=True,
@@ -168,14 +182,14 @@ def inputs_of(name):
     if name.startswith("backward_2d"):
         w, dy = wl.backward_2d(0)
         return dy, w
-    if name == "llama7b_fused_out_q":
+    if name in ("llama7b_fused_out_q", "llama7b_fused_quantize_a"):
         x, w, _ = wl.llama_linear(0)
         return x, w
     if name == "backward_dw_colwise":
         return wl.backward_dw(0)  # dY [tokens, 4096], X [tokens, 4096]
     if name == "forward_2d_transposed":
         return wl.forward_2d(0)  # X [8192, 4096], W [4096 (K), 4096 (N)]
-    return wl.nvfp4_4over6(0)
+    return wl.nvfp4_4over6(0)  # nvfp4_4over6, _lds and _given
 
 
 def given_scale(bits) -> float:
@@ -596,6 +610,13 @@ def main():
     qb = [fp4.empty_qtensor(N, K, pb, dev) for _ in range(args.copies)]
     cs = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(args.copies)]
     transposed_b = bool(wk.get("transposed_b"))
+    fused_a = bool(wk.get("fused_a"))
+    wsf = None
+    if fused_a:
+        import ctypes
+        bc = qb[0].c()
+        wsf = torch.empty(fp4.lib().fp4_gemm_quantize_a_workspace_bytes(M, ctypes.byref(bc)), dtype=torch.uint8,
+                          device=dev)
     if transposed_b:  # W [K, N] quantized once as stored (2D tiles); each step re-lays it out as W^T
         qw_stored = [fp4.quantize(Bs[j], pb) for j in range(args.copies)]
         torch.cuda.synchronize()
@@ -622,8 +643,9 @@ def main():
     if nb:
         wsb = torch.empty(nb, dtype=torch.uint8, device=dev)
     nb = fp4.gemm_workspace_bytes(qa[0], qb[0])
-    if nb:
+    if nb and not wk.get("nv_lds"):
         wsg = torch.empty(nb, dtype=torch.uint8, device=dev)
+    use_ws = not wk.get("nv_lds")
 
     # Timing events on the launch stream: one before each step's quantize and one between its
     # quantize and GEMM; a GEMM ends where the next step's first event is recorded (plus one after
@@ -637,6 +659,8 @@ def main():
         elif transposed_b:
             fp4.transpose_2d(qw_stored[j], out=qb[j])
             quantize_one(As[j], pa, out=qa[j], workspace=wsa)
+        elif fused_a:  # only W here: X is rotated and quantized by the GEMM launch itself
+            quantize_one(Bs[j], pb, out=qb[j], workspace=wsb)
         else:
             quantize_one(As[j], pa, out=qa[j], workspace=wsa,
                          tensor_scale=qa[j].tensor_scale if ga is not None else None)
@@ -646,8 +670,10 @@ def main():
             ev[2 * i + 1].record()
         if oq is not None:
             fp4.gemm(qa[j], qb[j], out=cs[j], workspace=wsg, out_q=oq, q_out=cq[j])
+        elif fused_a:
+            fp4.gemm_quantize_a(As[j], pa, qb[j], out=cs[j], a_out=qa[j], workspace=wsf)
         else:
-            fp4.gemm(qa[j], qb[j], out=cs[j], workspace=wsg)
+            fp4.gemm(qa[j], qb[j], out=cs[j], workspace=wsg, use_workspace=use_ws)
 
     # The GPU's clocks ramp up over the first tens of milliseconds of sustained work (a step runs
     # ~15 % slower at first): run the step untimed for --settle seconds before the warm-up steps,
@@ -682,6 +708,8 @@ def main():
         return rows * K * 2 + cb + sb
 
     bytes_q = qbytes(M, pa) + qbytes(N, pb)
+    if fused_a:  # the timed quantize launch is W's alone
+        bytes_q = qbytes(N, pb)
     if transposed_b:  # the re-layout reads and writes W's codes and scales once
         cbw, sbw, _ = fp4.buffer_sizes(N, K, pb)
         bytes_q = qbytes(M, pa) + 2 * (cbw + sbw)
@@ -713,6 +741,7 @@ def main():
                      "us": round(tq * 1e6, 2), "bytes": int(bytes_q),
                      "launches": ("one batched k_segment launch for A and B" if wk["batched"]
                                   else "quantize of A + the 2D re-layout of B's codes" if transposed_b
+                                  else "W alone (X is quantized inside the GEMM launch)" if fused_a
                                   else "separate launches for A and B")
                      + (", column-wise" if colwise else "") + (", given tensor scales" if ga is not None else "")},
         "gemm": {"TFLOP/s": round(gemm_tflops, 2), "frac": round(gemm_tflops / peak, 4),

@@ -480,7 +480,11 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
             c_dtype = FP4_DT_BF16;  // selects the kernel variant only; nothing is stored
             ldc = N;
         }
-        const int64_t need = gemm_ws(A, B, kind);
+        int64_t need = gemm_ws(A, B, kind);
+        // NVFP4 without a workspace: the FP8 re-expression happens in LDS (256 x 256 tile shapes)
+        const bool nv_in_lds = kind == 2 && !workspace && ws_bytes == 0 && M >= 256 && N >= 256 &&
+                               M * (K / 2) < (int64_t(1) << 31) && N * (K / 2) < (int64_t(1) << 31);
+        if (nv_in_lds) need = 0;
         if (need && (!workspace || ws_bytes < need)) return FP4_ERR_WORKSPACE;
         if (need && !aligned(workspace, 256)) return FP4_ERR_ALIGNMENT;
 
@@ -511,7 +515,7 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
             C_q->tensor_scale = nullptr;
             C_q->p = *out_q;
         }
-        if (kind == 2) {
+        if (kind == 2 && !nv_in_lds) {
             auto r = [](int64_t x) { return (x + 255) / 256 * 256; };
             uint8_t* w = reinterpret_cast<uint8_t*>(workspace);
             g.a8 = w;
@@ -523,6 +527,90 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
             g.sb8 = w;
         }
         return hip_status(launch_gemm(g, kind, c_dtype, fq ? 1 : 0, reinterpret_cast<hipStream_t>(stream)));
+    } catch (...) {
+        return FP4_ERR_INTERNAL;
+    }
+}
+
+int64_t fp4_gemm_quantize_a_workspace_bytes(int64_t M, const fp4_qtensor* B) {
+    if (M <= 0 || !B) return -1;
+    return 256;  // a counter and a status word
+}
+
+int fp4_gemm_quantize_a(const void* a, int32_t a_dtype, int64_t M, int64_t lda, const fp4_qparams* pa,
+                        fp4_qtensor* A_q, const fp4_qtensor* B, void* C, int32_t c_dtype, int64_t ldc,
+                        void* workspace, int64_t ws_bytes, void* stream) {
+    try {
+        if (!a || !pa || !A_q || !B || !C) return FP4_ERR_INVALID_ARG;
+        int rc = check_operand(B);
+        if (rc != FP4_OK) return rc;
+        const int64_t K = B->cols, N = B->rows;
+        Layout lay;
+        if ((rc = check_params(M, K, pa, &lay)) != FP4_OK) return rc;
+        // A: MXFP4 groups along K (E8M0 floor / ceil, nearest even or stochastic), rotated like B
+        if (pa->elem != FP4_ELEM_E2M1 || lay != L_SEG1D || pa->block_cols != 32 || scale_class(pa->scale_mode) != SC_E8M0)
+            return FP4_ERR_UNSUPPORTED;
+        if (pa->hadamard_n > 128) return FP4_ERR_UNSUPPORTED;
+        if (pa->hadamard_n != B->p.hadamard_n) return FP4_ERR_INVALID_ARG;
+        if (a_dtype != FP4_DT_F32 && a_dtype != FP4_DT_BF16) return FP4_ERR_INVALID_ARG;
+        if (c_dtype != FP4_DT_F32 && c_dtype != FP4_DT_BF16) return FP4_ERR_INVALID_ARG;
+        if (lda < K || ldc < N) return FP4_ERR_INVALID_ARG;
+        if (!A_q->codes || !A_q->scales) return FP4_ERR_INVALID_ARG;
+        if (A_q->codes == a || A_q->scales == a || A_q->codes == A_q->scales) return FP4_ERR_INVALID_ARG;
+        const int esz = a_dtype == FP4_DT_BF16 ? 2 : 4;
+        if (!aligned(a, 16) || (lda * esz) % 16 || !aligned(A_q->codes, 16) || !aligned(A_q->scales, 8) ||
+            !aligned(C, 16))
+            return FP4_ERR_ALIGNMENT;
+        if (lda != K && !pitch_ok(lda, esz)) return FP4_ERR_UNSUPPORTED;
+        fp4_qtensor Aq = *A_q;
+        Aq.rows = M;
+        Aq.cols = K;
+        Aq.tensor_scale = nullptr;
+        Aq.p = *pa;
+        int b2d;
+        if (gemm_kind(&Aq, B, &b2d) != 0) return FP4_ERR_UNSUPPORTED;  // B must be MXFP4 (1 x 32 or 2D)
+        if (K % 128) return FP4_ERR_UNSUPPORTED;
+        const int64_t need = fp4_gemm_quantize_a_workspace_bytes(M, B);
+        if (!workspace || ws_bytes < need) return FP4_ERR_WORKSPACE;
+        if (!aligned(workspace, 4)) return FP4_ERR_ALIGNMENT;
+
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        const bool fused = M >= 256 && N >= 256 && K % 256 == 0 && M * (K / 2) < (int64_t(1) << 31) &&
+                           N * (K / 2) < (int64_t(1) << 31);
+        // describe what is written into A_q
+        A_q->rows = M;
+        A_q->cols = K;
+        A_q->tensor_scale = nullptr;
+        A_q->p = *pa;
+        if (!fused) {  // shapes outside the 256 x 256 tile path: the quantize launch, then the GEMM
+            rc = fp4_quantize(a, a_dtype, M, K, lda, pa, A_q->codes, A_q->scales, nullptr, nullptr, 0, stream);
+            if (rc != FP4_OK) return rc;
+            return fp4_gemm(A_q, B, C, c_dtype, ldc, nullptr, nullptr, nullptr, 0, stream);
+        }
+        SegArgs sa{};
+        sa.x = a;
+        sa.rows = M;
+        sa.cols = K;
+        sa.ldx = lda;
+        sa.nseg = M * (K / 32);
+        sa.codes = reinterpret_cast<uint8_t*>(A_q->codes);
+        sa.scales = A_q->scales;
+        sa.seed = pa->seed;
+        sa.ceil_rule = pa->scale_mode == FP4_SCALE_E8M0_CEIL;
+        GemmArgs g{};
+        g.a = reinterpret_cast<const uint8_t*>(A_q->codes);
+        g.b = reinterpret_cast<const uint8_t*>(B->codes);
+        g.sa = reinterpret_cast<const uint8_t*>(A_q->scales);
+        g.sb = reinterpret_cast<const uint8_t*>(B->scales);
+        g.M = M;
+        g.N = N;
+        g.K = K;
+        g.c = C;
+        g.ldc = ldc;
+        g.b_2d = b2d;
+        return hip_status(launch_gemm_fused_a(g, sa, a_dtype, pa->hadamard_n,
+                                              pa->round_mode == FP4_ROUND_SR ? RND_SR : RND_RNE, c_dtype,
+                                              reinterpret_cast<uint32_t*>(workspace), s));
     } catch (...) {
         return FP4_ERR_INTERNAL;
     }

@@ -110,6 +110,12 @@ struct GemmArgs {
 hipError_t launch_nv_to_fp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                             uint8_t* out, uint8_t* out_scales, hipStream_t s);
 
+// MXFP4 GEMM (256 x 256 tile path) whose A operand is rotated (hn along K) and quantized (E8M0,
+// E2M1, rnd) from `a` inside the same launch; g.a / g.sa are a's codes / scales outputs. ws: at
+// least 2 words (a counter and a status word, cleared by the launch).
+hipError_t launch_gemm_fused_a(const GemmArgs& g, const SegArgs& a, int in_dtype, int hn, int rnd, int c_dtype,
+                               uint32_t* ws, hipStream_t s);
+
 // kind: 0 MXFP4, 1 MXFP8, 2 NVFP4 (via the FP8 rescale)
 hipError_t launch_gemm(const GemmArgs& g, int kind, int c_dtype, int fused_q, hipStream_t s);
 

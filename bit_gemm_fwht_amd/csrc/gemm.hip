@@ -31,6 +31,7 @@
 #include "device.h"
 #include "fp4_internal.h"
 #include "quant_block.h"
+#include "segment.h"
 
 namespace bgf {
 
@@ -325,23 +326,240 @@ __device__ __forceinline__ void wait_lgkm0() {
     __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
 }
 
-template <bool FP8, bool B2D, int OUT, bool NVG, int FQ>
-__global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
-    using C = Big<FP8>;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int wm = wave >> 2, wn = wave & 3;
+// ---------------------------------------------------------------------------------------------
+// NVFP4 -> MXFP8 re-expression of one 32-wide K group of a row: q holds its 32 E2M1 codes (element
+// k in nibble k % 8 of word k / 8), s01 its two E4M3 block scales (byte 0: elements 0-15). With S
+// the larger block scale, E is the smallest exponent with 448 * 2^E >= 6 S, and every element
+// becomes E4M3(val(q) * s_blk * 2^-E): val(q) * s_blk is exact in fp32 and the scaled convert
+// divides it by 2^E exactly before rounding to nearest even. o: 32 E4M3 bytes in element order.
+// Returns the E8M0 code E + 127 (E = -127 for S = 0, every element then 0).
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t nv_group_to_fp8(const u32x4 q, uint32_t s01, uint32_t (&o)[8]) {
+    const float s0 = e4m3_value(s01 & 0x7Fu), s1 = e4m3_value((s01 >> 8) & 0x7Fu);
+    const float S = fmaxf(s0, s1);
+    // E = smallest exponent with 448 * 2^E >= 6 S (6 S is exact in fp32)
+    const int E = e8m0_exp<8, 0x600000u>(6.0f * S, true);
+    const float sc = E > -127 ? pow2f(E) : 1.0f;  // S = 0: every product is 0
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float sb = w < 2 ? s0 : s1;
+        const v2f p0 = fp4x2_to_f32<0>(q[w]), p1 = fp4x2_to_f32<1>(q[w]);
+        const v2f p2 = fp4x2_to_f32<2>(q[w]), p3 = fp4x2_to_f32<3>(q[w]);
+        uint32_t r0 = 0u, r1 = 0u;
+        r0 = cvt_fp8x2<false>(r0, p0[0] * sb, p0[1] * sb, sc);
+        r0 = cvt_fp8x2<true>(r0, p1[0] * sb, p1[1] * sb, sc);
+        r1 = cvt_fp8x2<false>(r1, p2[0] * sb, p2[1] * sb, sc);
+        r1 = cvt_fp8x2<true>(r1, p3[0] * sb, p3[1] * sb, sc);
+        o[2 * w] = r0;
+        o[2 * w + 1] = r1;
+    }
+    return (uint32_t)(E + 127);
+}
 
-    // tile assignment: XCD-contiguous runs, grouped by 4 tile rows
-    const int ntm = (int)((g.M + C::TM - 1) / C::TM), ntn = (int)((g.N + C::TN - 1) / C::TN);
+// Tile coordinates of work item b (a workgroup index of the one-tile-per-workgroup launch): the
+// workgroups of each of the 8 XCDs (which receive ids round-robin) own a contiguous run of tiles,
+// walked in groups of 4 tile rows for L2 reuse.
+__device__ __forceinline__ void big_tile_coords(int b, int ntm, int ntn, int& tm, int& tn) {
     const int T = ntm * ntn;
-    int b = blockIdx.x;
     if (T % 8 == 0) b = (b % 8) * (T / 8) + b / 8;
     const int GM = 4;
     const int grp = b / (GM * ntn), first = grp * GM;
     const int gs = (ntm - first) < GM ? (ntm - first) : GM;
-    const int tm = first + (b % (GM * ntn)) % gs, tn = (b % (GM * ntn)) / gs;
+    tm = first + (b % (GM * ntn)) % gs;
+    tn = (b % (GM * ntn)) / gs;
+}
+
+// One 256 x 256 tile of C (tile row tm, tile column tn) by the whole 512-thread workgroup, LDS
+// `smem` of Big<FP8>::NST stages; every thread must call it. Leaves the LDS free (every copy into
+// it has landed) but does not end with a barrier.
+// Epilogue of a 256 x 256 tile: the accumulators (lane layout of the 32x32x64 MFMA tiles of
+// big_tile) to C, and to C_q when FQ; uses the first 256 * 528 bytes of `smem`, which must be free
+// (no copy into it still in flight). Every thread of the workgroup must call it.
+template <bool FP8, int OUT, bool NVG, int FQ>
+__device__ __forceinline__ void big_epilogue(const GemmArgs& g, v16f (&acc)[Big<FP8>::WTN][Big<FP8>::WTM], int64_t m0,
+                                             int64_t n0, uint8_t* smem) {
+    using C = Big<FP8>;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int wm = wave >> 2, wn = wave & 3;
+    const int fr = lane & 31, fg = lane >> 5;
+    // Epilogue, staged through LDS so that every global store writes whole 16-byte pieces of a
+    // row and consecutive lanes cover consecutive bytes. Lane (fr, fg) holds, for 4-register group
+    // q of tile (im, in), C[m][n .. n+3] with m = wm*128 + 32 im + fr and
+    // n = wn*64 + 32 in + 8 q + 4 fg. A pass stages 256 rows x 512 bytes: bf16 output in one pass
+    // (all 256 columns), fp32 output in two (pass p holds columns wn*64 + 32 p + [0, 32) of each
+    // wave column wn, i.e. four 128-byte runs per row).
+    constexpr int EP = 528;                       // staged row pitch (512 B + 16 B of padding)
+    static_assert(256 * EP <= C::NST * C::STAGE, "staging buffer exceeds the stage buffers");
+    constexpr int PASSES = OUT == DT_F32 ? 2 : 1;
+    float gscale = 1.0f;
+    if constexpr (NVG) gscale = (*g.ga) * (*g.gb);
+    // an opaque zero keeps the compiler from computing the output addresses before the main
+    // loop, where they would only add register pressure
+    int opaque_zero;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(opaque_zero));
+    const int64_t me0 = m0 + opaque_zero, ne0 = n0 + opaque_zero, ldc = g.ldc + opaque_zero;
+    char* const cbase = reinterpret_cast<char*>(g.c) + opaque_zero;
+    const int64_t Mx = g.M + opaque_zero, Nx = g.N + opaque_zero;
+    if constexpr (FQ != FQ_NONE) {
+        // fused output quantization, in two passes of 128 columns: the fp32 values (as an fp32 C
+        // would hold them) are staged in LDS, [256 rows][128] per pass (pass p holds tile columns
+        // [128 p, 128 p + 128), written by the four waves with wn / 2 = p), then one thread per
+        // 32-column group reads its group back, rotates it along N if asked (the four groups of a
+        // row are in consecutive lanes) and quantizes it with the rules of the quantize kernels
+        static_assert(C::WTN == 2 && C::NTH == 512, "two staged passes of 128 columns");
+        for (int p = 0; p < 2; ++p) {
+            barrier_only();  // every wave is done with the stage buffers / the last pass
+            if ((wn >> 1) == p) {  // wave-uniform
+#pragma unroll
+                for (int in = 0; in < C::WTN; ++in)
+#pragma unroll
+                    for (int im = 0; im < C::WTM; ++im) {
+                        const int row = wm * 128 + 32 * im + fr;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            f32x4 v;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) v[i] = NVG ? acc[in][im][4 * q + i] * gscale : acc[in][im][4 * q + i];
+                            *reinterpret_cast<f32x4*>(smem + row * EP + 4 * (64 * (wn & 1) + 32 * in + 8 * q + 4 * fg)) = v;
+                        }
+                    }
+            }
+            wait_lgkm0();
+            barrier_only();
+#pragma unroll 1
+            for (int t = tid; t < 256 * 4; t += C::NTH) {  // two sweeps, every lane in both
+                const int r = t >> 2, j = t & 3;  // row, staged group
+                const int64_t m = me0 + r, nb = ne0 + 128 * p + 32 * j;
+                float v[32];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(smem + r * EP + 4 * (32 * j + 4 * c));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[4 * c + i] = x[i];
+                }
+                fwht_groups(v, g.q_hn);
+                uint32_t out[8];
+                const float amax = block_amax<32, 0>(v);
+                uint32_t sbyte;
+                const SrSource sr{g.q_seed, (uint64_t)(m * Nx + nb)};
+                if constexpr (FQ == FQ_SR) {
+                    sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, sr, out)
+                                                  : e8m0_block<ELEM_E4M3, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, sr, out);
+                } else {
+                    sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_RNE, 32, 0>(v, amax, g.q_ceil != 0, sr, out)
+                                                  : e8m0_block<ELEM_E4M3, RND_RNE, 32, 0>(v, amax, g.q_ceil != 0, sr, out);
+                }
+                if (m < Mx && nb < Nx) {
+                    if (g.q_elem == ELEM_E2M1) {
+                        *reinterpret_cast<u32x4*>(g.qcodes + m * (Nx / 2) + nb / 2) = (u32x4){out[0], out[1], out[2], out[3]};
+                    } else {
+                        u32x4* d = reinterpret_cast<u32x4*>(g.qcodes + m * Nx + nb);
+                        d[0] = (u32x4){out[0], out[1], out[2], out[3]};
+                        d[1] = (u32x4){out[4], out[5], out[6], out[7]};
+                    }
+                    g.qscales[m * (Nx / 32) + nb / 32] = (uint8_t)sbyte;
+                }
+            }
+            if (g.c) {
+                // C from the same staged values: 16-byte output pieces, staged column c of a row
+                // is tile column 128 p + c
+                constexpr int ESZ = OUT == DT_F32 ? 4 : 2, EPC = 16 / ESZ, PPR = 128 / EPC;
+                const bool vec_ok = ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) && ((ldc * ESZ) % 16 == 0);
+#pragma unroll 1
+                for (int t = tid; t < 256 * PPR; t += C::NTH) {
+                    const int r = t / PPR, c = (t % PPR) * EPC;
+                    const int64_t m = me0 + r, n = ne0 + 128 * p + c;
+                    if (m >= Mx) continue;
+                    const float* src = reinterpret_cast<const float*>(smem + r * EP) + c;
+                    u32x4 val;
+                    if constexpr (OUT == DT_F32) {
+                        val = *reinterpret_cast<const u32x4*>(src);
+                    } else {
+                        const f32x4 a = *reinterpret_cast<const f32x4*>(src), b = *reinterpret_cast<const f32x4*>(src + 4);
+                        val = (u32x4){pack_bf16x2_rne(a[0], a[1]), pack_bf16x2_rne(a[2], a[3]),
+                                      pack_bf16x2_rne(b[0], b[1]), pack_bf16x2_rne(b[2], b[3])};
+                    }
+                    char* cp = cbase + (m * ldc + n) * ESZ;
+                    if (vec_ok && n + EPC <= Nx) {
+                        *reinterpret_cast<u32x4*>(cp) = val;
+                    } else {
+                        for (int i = 0; i < EPC; ++i) {
+                            if (n + i < Nx) {
+                                if constexpr (OUT == DT_F32)
+                                    reinterpret_cast<uint32_t*>(cp)[i] = val[i];
+                                else
+                                    reinterpret_cast<uint16_t*>(cp)[i] = (uint16_t)(val[i >> 1] >> (16 * (i & 1)));
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        return;
+    }
+    constexpr int ESZ = OUT == DT_F32 ? 4 : 2;
+    // 16-byte stores need a 16-byte aligned row start
+    const bool vec_ok = ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) && ((ldc * ESZ) % 16 == 0);
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        barrier_only();  // every wave is done reading the stage buffers / the last pass
+#pragma unroll
+        for (int im = 0; im < C::WTM; ++im)
+#pragma unroll
+            for (int inn = 0; inn < (OUT == DT_F32 ? 1 : C::WTN); ++inn) {
+                const int in = OUT == DT_F32 ? p : inn;
+                const int row = wm * 128 + 32 * im + fr;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float v[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = NVG ? acc[in][im][4 * q + i] * gscale : acc[in][im][4 * q + i];
+                    if constexpr (OUT == DT_F32) {
+                        const int col = wn * 32 + 8 * q + 4 * fg;
+                        *reinterpret_cast<f32x4*>(smem + row * EP + 4 * col) = (f32x4){v[0], v[1], v[2], v[3]};
+                    } else {
+                        const int col = wn * 64 + 32 * in + 8 * q + 4 * fg;
+                        *reinterpret_cast<u32x2*>(smem + row * EP + 2 * col) =
+                            (u32x2){pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3])};
+                    }
+                }
+            }
+        wait_lgkm0();
+        barrier_only();
+        // 32 lanes per row, 16 rows per sweep of the workgroup
+        const int c16 = tid & 31;
+        const int64_t n = OUT == DT_F32 ? ne0 + (c16 >> 3) * 64 + 32 * p + 4 * (c16 & 7) : ne0 + 8 * c16;
+        constexpr int EPC = 16 / ESZ;  // elements per 16-byte piece
+#pragma unroll 4
+        for (int r = tid >> 5; r < 256; r += C::NTH / 32) {
+            const int64_t m = me0 + r;
+            if (m >= Mx) break;
+            const u32x4 val = *reinterpret_cast<const u32x4*>(smem + r * EP + 16 * c16);
+            char* cp = cbase + (m * ldc + n) * ESZ;
+            if (vec_ok && n + EPC <= Nx) {
+                *reinterpret_cast<u32x4*>(cp) = val;
+            } else {
+#pragma unroll
+                for (int i = 0; i < EPC; ++i) {
+                    if (n + i < Nx) {
+                        if constexpr (OUT == DT_F32)
+                            reinterpret_cast<uint32_t*>(cp)[i] = val[i];
+                        else
+                            reinterpret_cast<uint16_t*>(cp)[i] = (uint16_t)(val[i >> 1] >> (16 * (i & 1)));
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <bool FP8, bool B2D, int OUT, bool NVG, int FQ>
+__device__ __forceinline__ void big_tile(const GemmArgs& g, int tm, int tn, uint8_t* smem) {
+    using C = Big<FP8>;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int wm = wave >> 2, wn = wave & 3;
     const int64_t m0 = (int64_t)tm * C::TM, n0 = (int64_t)tn * C::TN;
 
     const int64_t rowbytes = FP8 ? g.K : g.K / 2;
@@ -533,175 +751,314 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
     }
     wait_vm<0>();  // the dummy stage's zero-fill has landed before the LDS is reused
 
-    // Epilogue, staged through LDS so that every global store writes whole 16-byte pieces of a
-    // row and consecutive lanes cover consecutive bytes. Lane (fr, fg) holds, for 4-register group
-    // q of tile (im, in), C[m][n .. n+3] with m = wm*128 + 32 im + fr and
-    // n = wn*64 + 32 in + 8 q + 4 fg. A pass stages 256 rows x 512 bytes: bf16 output in one pass
-    // (all 256 columns), fp32 output in two (pass p holds columns wn*64 + 32 p + [0, 32) of each
-    // wave column wn, i.e. four 128-byte runs per row).
-    constexpr int EP = 528;                       // staged row pitch (512 B + 16 B of padding)
-    static_assert(256 * EP <= C::NST * C::STAGE, "staging buffer exceeds the stage buffers");
-    constexpr int PASSES = OUT == DT_F32 ? 2 : 1;
-    float gscale = 1.0f;
-    if constexpr (NVG) gscale = (*g.ga) * (*g.gb);
-    // an opaque zero keeps the compiler from computing the output addresses before the main
-    // loop, where they would only add register pressure
-    int opaque_zero;
-    asm volatile("s_mov_b32 %0, 0" : "=s"(opaque_zero));
-    const int64_t me0 = m0 + opaque_zero, ne0 = n0 + opaque_zero, ldc = g.ldc + opaque_zero;
-    char* const cbase = reinterpret_cast<char*>(g.c) + opaque_zero;
-    const int64_t Mx = g.M + opaque_zero, Nx = g.N + opaque_zero;
-    if constexpr (FQ != FQ_NONE) {
-        // fused output quantization, in two passes of 128 columns: the fp32 values (as an fp32 C
-        // would hold them) are staged in LDS, [256 rows][128] per pass (pass p holds tile columns
-        // [128 p, 128 p + 128), written by the four waves with wn / 2 = p), then one thread per
-        // 32-column group reads its group back, rotates it along N if asked (the four groups of a
-        // row are in consecutive lanes) and quantizes it with the rules of the quantize kernels
-        static_assert(C::WTN == 2 && C::NTH == 512, "two staged passes of 128 columns");
-        for (int p = 0; p < 2; ++p) {
-            barrier_only();  // every wave is done with the stage buffers / the last pass
-            if ((wn >> 1) == p) {  // wave-uniform
+    big_epilogue<FP8, OUT, NVG, FQ>(g, acc, m0, n0, smem);
+}
+
+// ---------------------------------------------------------------------------------------------
+// NVFP4 x NVFP4 with the FP8 re-expression done in LDS (no pre-pass, no workspace): per 128-deep K
+// stage the workgroup copies the raw E2M1 codes (64 B per row) and E4M3 block scales (8 B per row)
+// of its 256 A rows and 256 B rows straight into LDS (two raw stages in a ring, 36 KB each), then
+// every thread re-expresses one row's four 32-wide groups (nv_group_to_fp8, the same arithmetic as
+// the pre-pass) into a single FP8 stage laid out exactly as the MXFP8 tiles' (66 KB), and the
+// FP8 scaled MFMAs run on it as in big_tile. Two barriers per stage: one before the conversion (raw
+// stage landed, FP8 stage free), one before the MFMAs (FP8 stage complete); the next raw stage's
+// copies are in flight across both.
+// ---------------------------------------------------------------------------------------------
+struct NvLds {
+    static constexpr int ROWS = 512;                 // A's 256 tile rows, then B's 256
+    static constexpr int CB = 64;                    // E2M1 code bytes per row per stage
+    static constexpr int SBY = 8;                    // E4M3 block scales per row per stage
+    static constexpr int RAW_SCALES = 0, RAW_CODES = ROWS * SBY;
+    static constexpr int RAW = ROWS * (CB + SBY);    // one raw stage
+    static constexpr int FP8 = 2 * RAW;              // the FP8 stage, after the two raw stages
+    static constexpr int LDS = FP8 + Big<true>::STAGE;
+};
+
+template <int OUT, int FQ>
+__device__ __forceinline__ void nv_lds_tile(const GemmArgs& g, int tm, int tn, uint8_t* smem) {
+    using C = Big<true>;
+    using NL = NvLds;
+    static_assert(NL::LDS <= 160 * 1024, "LDS budget");
+    static_assert(256 * 528 <= NL::LDS, "epilogue staging");
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int wm = wave >> 2, wn = wave & 3;
+    const int64_t m0 = (int64_t)tm * C::TM, n0 = (int64_t)tn * C::TN;
+    const int64_t rowbytes = g.K / 2, sgroups = g.K / 16;
+    const int KT = (int)(g.K / C::KSTEP);
+
+    // raw copies: wave w moves rows 64 w .. 64 w + 63 of the 512 (A's for w < 4, else B's); rows past
+    // M or N lie past the buffers' extents and read as zeros (their scales 0, so their FP8 values 0)
+    const bool isB = wave >= 4;
+    const int64_t orow0 = (isB ? n0 : m0) + 64 * (wave & 3);
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(isB ? g.b : g.a), (short)0, (int)((isB ? g.N : g.M) * rowbytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(isB ? g.sb : g.sa), (short)0, (int)((isB ? g.N : g.M) * sgroups), 0x00020000);
+    // code copy i: rows 16 i + lane / 4 of the wave's 64, LDS slot lane % 4 of the row holding
+    // chunk (lane % 4) ^ ((row / 4) % 4), so that a thread's reads of its row's chunks spread over
+    // the banks; scale copy j: rows 32 j + lane / 2, dword lane % 2
+    int voC[4], voS[2];
 #pragma unroll
-                for (int in = 0; in < C::WTN; ++in)
-#pragma unroll
-                    for (int im = 0; im < C::WTM; ++im) {
-                        const int row = wm * 128 + 32 * im + fr;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            f32x4 v;
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) v[i] = NVG ? acc[in][im][4 * q + i] * gscale : acc[in][im][4 * q + i];
-                            *reinterpret_cast<f32x4*>(smem + row * EP + 4 * (64 * (wn & 1) + 32 * in + 8 * q + 4 * fg)) = v;
-                        }
-                    }
-            }
-            wait_lgkm0();
-            barrier_only();
-#pragma unroll 1
-            for (int t = tid; t < 256 * 4; t += C::NTH) {  // two sweeps, every lane in both
-                const int r = t >> 2, j = t & 3;  // row, staged group
-                const int64_t m = me0 + r, nb = ne0 + 128 * p + 32 * j;
-                float v[32];
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const f32x4 x = *reinterpret_cast<const f32x4*>(smem + r * EP + 4 * (32 * j + 4 * c));
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) v[4 * c + i] = x[i];
-                }
-                fwht_groups(v, g.q_hn);
-                uint32_t out[8];
-                const float amax = block_amax<32, 0>(v);
-                uint32_t sbyte;
-                const SrSource sr{g.q_seed, (uint64_t)(m * Nx + nb)};
-                if constexpr (FQ == FQ_SR) {
-                    sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, sr, out)
-                                                  : e8m0_block<ELEM_E4M3, RND_SR, 32, 0>(v, amax, g.q_ceil != 0, sr, out);
-                } else {
-                    sbyte = g.q_elem == ELEM_E2M1 ? e8m0_block<ELEM_E2M1, RND_RNE, 32, 0>(v, amax, g.q_ceil != 0, sr, out)
-                                                  : e8m0_block<ELEM_E4M3, RND_RNE, 32, 0>(v, amax, g.q_ceil != 0, sr, out);
-                }
-                if (m < Mx && nb < Nx) {
-                    if (g.q_elem == ELEM_E2M1) {
-                        *reinterpret_cast<u32x4*>(g.qcodes + m * (Nx / 2) + nb / 2) = (u32x4){out[0], out[1], out[2], out[3]};
-                    } else {
-                        u32x4* d = reinterpret_cast<u32x4*>(g.qcodes + m * Nx + nb);
-                        d[0] = (u32x4){out[0], out[1], out[2], out[3]};
-                        d[1] = (u32x4){out[4], out[5], out[6], out[7]};
-                    }
-                    g.qscales[m * (Nx / 32) + nb / 32] = (uint8_t)sbyte;
-                }
-            }
-            if (g.c) {
-                // C from the same staged values: 16-byte output pieces, staged column c of a row
-                // is tile column 128 p + c
-                constexpr int ESZ = OUT == DT_F32 ? 4 : 2, EPC = 16 / ESZ, PPR = 128 / EPC;
-                const bool vec_ok = ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) && ((ldc * ESZ) % 16 == 0);
-#pragma unroll 1
-                for (int t = tid; t < 256 * PPR; t += C::NTH) {
-                    const int r = t / PPR, c = (t % PPR) * EPC;
-                    const int64_t m = me0 + r, n = ne0 + 128 * p + c;
-                    if (m >= Mx) continue;
-                    const float* src = reinterpret_cast<const float*>(smem + r * EP) + c;
-                    u32x4 val;
-                    if constexpr (OUT == DT_F32) {
-                        val = *reinterpret_cast<const u32x4*>(src);
-                    } else {
-                        const f32x4 a = *reinterpret_cast<const f32x4*>(src), b = *reinterpret_cast<const f32x4*>(src + 4);
-                        val = (u32x4){pack_bf16x2_rne(a[0], a[1]), pack_bf16x2_rne(a[2], a[3]),
-                                      pack_bf16x2_rne(b[0], b[1]), pack_bf16x2_rne(b[2], b[3])};
-                    }
-                    char* cp = cbase + (m * ldc + n) * ESZ;
-                    if (vec_ok && n + EPC <= Nx) {
-                        *reinterpret_cast<u32x4*>(cp) = val;
-                    } else {
-                        for (int i = 0; i < EPC; ++i) {
-                            if (n + i < Nx) {
-                                if constexpr (OUT == DT_F32)
-                                    reinterpret_cast<uint32_t*>(cp)[i] = val[i];
-                                else
-                                    reinterpret_cast<uint16_t*>(cp)[i] = (uint16_t)(val[i >> 1] >> (16 * (i & 1)));
-                            }
-                        }
-                    }
-                }
-            }
-        }
-        return;
+    for (int i = 0; i < 4; ++i) {
+        const int ro = 16 * i + (lane >> 2), q = (lane & 3) ^ ((lane >> 4) & 3);
+        voC[i] = (int)((orow0 + ro) * rowbytes + 16 * q);
     }
-    constexpr int ESZ = OUT == DT_F32 ? 4 : 2;
-    // 16-byte stores need a 16-byte aligned row start
-    const bool vec_ok = ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) && ((ldc * ESZ) % 16 == 0);
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-        barrier_only();  // every wave is done reading the stage buffers / the last pass
+    for (int j = 0; j < 2; ++j) voS[j] = (int)((orow0 + 32 * j + (lane >> 1)) * sgroups + 4 * (lane & 1));
+    auto issue_raw = [&](int kt) {
+        uint8_t* st = smem + (kt & 1) * NL::RAW;
 #pragma unroll
-        for (int im = 0; im < C::WTM; ++im)
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_ptr_t)(st + NL::RAW_CODES + (64 * wave + 16 * i) * NL::CB),
+                                                     16, voC[i], kt * NL::CB, 0, 0);
 #pragma unroll
-            for (int inn = 0; inn < (OUT == DT_F32 ? 1 : C::WTN); ++inn) {
-                const int in = OUT == DT_F32 ? p : inn;
-                const int row = wm * 128 + 32 * im + fr;
+        for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(st + NL::RAW_SCALES + (64 * wave + 32 * j) * NL::SBY),
+                                                     4, voS[j], kt * NL::SBY, 0, 0);
+    };
+    uint8_t* const fp8 = smem + NL::FP8;
+    // conversion: thread t re-expresses row t of the 512 (its four 32-wide groups)
+    auto convert = [&](int kt) {
+        const uint8_t* raw = smem + (kt & 1) * NL::RAW;
+        const int t = tid, row = t & 255;
+        const uint2 sc = *reinterpret_cast<const uint2*>(raw + NL::RAW_SCALES + t * NL::SBY);
+        uint8_t* dst = fp8 + (t < 256 ? C::OFF_A : C::OFF_B) + row * C::RB;
+        const int sw = chunk_swz(row);
+        uint32_t e = 0u;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float v[4];
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 q = *reinterpret_cast<const u32x4*>(raw + NL::RAW_CODES + t * NL::CB + 16 * (j ^ ((t >> 2) & 3)));
+            const uint32_t s01 = ((j < 2 ? sc.x : sc.y) >> (16 * (j & 1))) & 0xFFFFu;
+            uint32_t o[8];
+            e |= nv_group_to_fp8(q, s01, o) << (8 * j);
+            *reinterpret_cast<u32x4*>(dst + 16 * ((2 * j) ^ sw)) = (u32x4){o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<u32x4*>(dst + 16 * ((2 * j + 1) ^ sw)) = (u32x4){o[4], o[5], o[6], o[7]};
+        }
+        *reinterpret_cast<uint32_t*>(fp8 + (t < 256 ? 0 : C::OFF_SB) + row * C::SPR) = e;
+    };
+
+    v16f acc[C::WTN][C::WTM];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = NVG ? acc[in][im][4 * q + i] * gscale : acc[in][im][4 * q + i];
-                    if constexpr (OUT == DT_F32) {
-                        const int col = wn * 32 + 8 * q + 4 * fg;
-                        *reinterpret_cast<f32x4*>(smem + row * EP + 4 * col) = (f32x4){v[0], v[1], v[2], v[3]};
-                    } else {
-                        const int col = wn * 64 + 32 * in + 8 * q + 4 * fg;
-                        *reinterpret_cast<u32x2*>(smem + row * EP + 2 * col) =
-                            (u32x2){pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3])};
-                    }
+    for (int i = 0; i < C::WTN; ++i)
+#pragma unroll
+        for (int j = 0; j < C::WTM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // fragments as in big_tile (FP8: two 16-byte pieces per lane and 64-deep step)
+    const int fr = lane & 31, fg = lane >> 5;
+    const int sw = chunk_swz(fr);
+    int ch[C::NKK][2];
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) ch[kk][p] = 16 * ((4 * kk + 2 * p + fg) ^ sw);
+    const int aRow = C::OFF_A + (wm * 128 + fr) * C::RB, bRow = C::OFF_B + (wn * 64 + fr) * C::RB;
+    const int aScl = C::SPR * (wm * 128 + fr), bScl = C::OFF_SB + C::SPR * (wn * 64 + fr);
+    const int sshift = 8 * fg;
+    auto frag = [&](const uint8_t* p0, const uint8_t* p1) -> v8i {
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(p0);
+        const u32x4 x1 = *reinterpret_cast<const u32x4*>(p1);
+        return (v8i){(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+    };
+    auto load_frags = [&](int kk, v8i (&fa)[C::WTM], v8i (&fb)[C::WTN]) {
+#pragma unroll
+        for (int i = 0; i < C::WTM; ++i)
+            fa[i] = frag(fp8 + aRow + 32 * C::RB * i + ch[kk][0], fp8 + aRow + 32 * C::RB * i + ch[kk][1]);
+#pragma unroll
+        for (int i = 0; i < C::WTN; ++i)
+            fb[i] = frag(fp8 + bRow + 32 * C::RB * i + ch[kk][0], fp8 + bRow + 32 * C::RB * i + ch[kk][1]);
+    };
+    auto compute = [&]() {
+        int sa[C::WTM], sb[C::WTN];
+#pragma unroll
+        for (int i = 0; i < C::WTM; ++i) sa[i] = (int)(*reinterpret_cast<const uint32_t*>(fp8 + aScl + C::SPR * 32 * i) >> sshift);
+#pragma unroll
+        for (int i = 0; i < C::WTN; ++i) sb[i] = (int)(*reinterpret_cast<const uint32_t*>(fp8 + bScl + C::SPR * 32 * i) >> sshift);
+        v8i fa[2][C::WTM], fb[2][C::WTN];
+        load_frags(0, fa[0], fb[0]);
+#pragma unroll
+        for (int kk = 0; kk < C::NKK; ++kk) {
+            const int cur = kk & 1, nxt = cur ^ 1;
+            if (kk + 1 < C::NKK) load_frags(kk + 1, fa[nxt], fb[nxt]);
+#pragma unroll
+            for (int in = 0; in < C::WTN; ++in)
+#pragma unroll
+                for (int im = 0; im < C::WTM; ++im) {
+                    if (kk == 0)
+                        acc[in][im] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[cur][in], fa[cur][im], acc[in][im],
+                                                                                      0, 0, 0, sb[in], 0, sa[im]);
+                    else
+                        acc[in][im] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[cur][in], fa[cur][im], acc[in][im],
+                                                                                      0, 0, 2, sb[in], 2, sa[im]);
                 }
-            }
+        }
+    };
+
+    issue_raw(0);
+    for (int kt = 0; kt < KT; ++kt) {
+        wait_vm<0>();    // this wave's raw copies of stage kt have landed
+        barrier_only();  // ... and everyone's; the FP8 stage and raw stage kt + 1 are free
+        if (kt + 1 < KT) issue_raw(kt + 1);
+        convert(kt);
         wait_lgkm0();
-        barrier_only();
-        // 32 lanes per row, 16 rows per sweep of the workgroup
-        const int c16 = tid & 31;
-        const int64_t n = OUT == DT_F32 ? ne0 + (c16 >> 3) * 64 + 32 * p + 4 * (c16 & 7) : ne0 + 8 * c16;
-        constexpr int EPC = 16 / ESZ;  // elements per 16-byte piece
-#pragma unroll 4
-        for (int r = tid >> 5; r < 256; r += C::NTH / 32) {
-            const int64_t m = me0 + r;
-            if (m >= Mx) break;
-            const u32x4 val = *reinterpret_cast<const u32x4*>(smem + r * EP + 16 * c16);
-            char* cp = cbase + (m * ldc + n) * ESZ;
-            if (vec_ok && n + EPC <= Nx) {
-                *reinterpret_cast<u32x4*>(cp) = val;
-            } else {
-#pragma unroll
-                for (int i = 0; i < EPC; ++i) {
-                    if (n + i < Nx) {
-                        if constexpr (OUT == DT_F32)
-                            reinterpret_cast<uint32_t*>(cp)[i] = val[i];
-                        else
-                            reinterpret_cast<uint16_t*>(cp)[i] = (uint16_t)(val[i >> 1] >> (16 * (i & 1)));
-                    }
-                }
-            }
+        barrier_only();  // the FP8 stage is complete
+        compute();
+    }
+    wait_vm<0>();
+    big_epilogue<true, OUT, true, FQ>(g, acc, m0, n0, smem);
+}
+
+template <int OUT, int FQ>
+__global__ __launch_bounds__(512) void k_gemm_nv(GemmArgs g) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int ntm = (int)((g.M + 255) / 256), ntn = (int)((g.N + 255) / 256);
+    int tm, tn;
+    big_tile_coords(blockIdx.x, ntm, ntn, tm, tn);
+    nv_lds_tile<OUT, FQ>(g, tm, tn, smem);
+}
+
+template <bool FP8, bool B2D, int OUT, bool NVG, int FQ>
+__global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int ntm = (int)((g.M + 255) / 256), ntn = (int)((g.N + 255) / 256);
+    int tm, tn;
+    big_tile_coords(blockIdx.x, ntm, ntn, tm, tn);
+    big_tile<FP8, B2D, OUT, NVG, FQ>(g, tm, tn, smem);
+}
+
+// ---------------------------------------------------------------------------------------------
+// GEMM with the rotation and MX quantization of A fused in (bf16 / fp32 activations in; the QuTLASS
+// kernel list of the Quartet notes: rotation fused before the GEMM, no separate launch). One
+// persistent launch, every workgroup resident at once (a cooperative launch guarantees it):
+//  1. all workgroups rotate + quantize A [M, K] exactly as the quantize kernels do (one wave per
+//     64-segment wave tile, grid-stride), writing the caller's A codes and scales; then each
+//     workgroup publishes its part with one agent-scope release (the stores leave the XCD's L2);
+//  2. each workgroup waits (one agent-scope acquire, bounded spin) until every workgroup has
+//     published, then walks its tiles (b, b + G, ...) in the usual XCD-grouped order with the
+//     256 x 256 tile unchanged.
+// Measured at 4096 x 11008 x 4096 (X bf16, H_128): this launch takes 150-158 us against 13 us for
+// X's own quantize launch plus 111-122 us for the GEMM: the cooperative launch adds ~25 us, and
+// phase 1 runs at the GEMM's occupancy (8 waves per CU, against the quantize kernel's many), about
+// 2.5 us per wave tile and wave (four tiles' loads in flight per wave measured no faster). The
+// separate quantize stays the faster route; this one saves A's extra pass only where a caller needs
+// a single launch.
+// A is quantized once by the whole grid, not once per tile. The hand-over is grid-wide rather than
+// per tile row: an agent-scope acquire invalidates the XCD's L2 and a release writes it back, and
+// with one release per wave tile and one acquire per tile (each tile waiting only for its own tile
+// row) the 4096 x 11008 x 4096 product ran 3.3x slower; the first round of tiles needs rows of A
+// from every tile row anyway.
+// ---------------------------------------------------------------------------------------------
+struct FusedA {
+    SegArgs a;              // A's input and its codes / scales outputs (also g.a / g.sa)
+    uint32_t* done;         // workgroups that have published their part of A (cleared before)
+    uint32_t* status;       // bit 0 set if the wait gave up (results then invalid)
+    int64_t units;          // wave tiles of 64 segments covering A
+    int hn;                 // rotation of A along K (0, 16, 32, 64, 128)
+};
+
+__global__ void k_fill_u32(uint32_t* p, int n, uint32_t v) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+template <int IN, int RND, bool B2D, int OUT>
+__global__ __launch_bounds__(512) void k_gemm_fused_a(GemmArgs g, FusedA f) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    constexpr int P = SegIO<IN>::P;
+    // phase 1: A's wave tiles, each wave with its own LDS slice for the segment transposition
+    u32x4* lds = reinterpret_cast<u32x4*>(smem) + wave * 64 * P;
+    const int64_t nw = (int64_t)gridDim.x * 8;
+    for (int64_t u = (int64_t)blockIdx.x * 8 + wave; u < f.units; u += nw) {
+        const int64_t wbase = u * 64, seg = wbase + lane;
+        float v[32];
+        load_wave_segments_1d<IN>(f.a, wbase, lds, v);
+        fwht_groups(v, f.hn);
+        uint32_t out[8];
+        const SrSource sr{f.a.seed, (uint64_t)seg * 32u};
+        const uint32_t s = e8m0_block<ELEM_E2M1, RND, 32, 0>(v, block_amax<32, 0>(v), f.a.ceil_rule != 0, sr, out);
+        if (seg < f.a.nseg) {
+            reinterpret_cast<uint8_t*>(f.a.scales)[seg] = (uint8_t)s;
+            *reinterpret_cast<u32x4*>(f.a.codes + seg * 16) = (u32x4){out[0], out[1], out[2], out[3]};
         }
     }
+    __syncthreads();  // the workgroup's stores are done; every wave is done with its LDS slice
+    if (tid == 0) {
+        // release: the workgroup's stores reach memory beyond this XCD's L2 before the count
+        __hip_atomic_fetch_add(f.done, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        // every workgroup is resident and publishes before it waits, so the count arrives; the
+        // bound only keeps a broken launch from spinning for ever
+        for (uint32_t spin = 0;
+             __hip_atomic_load(f.done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x; ++spin) {
+            if (spin > (1u << 24)) {
+                atomicOr(f.status, 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    __syncthreads();
+    // phase 2: the tiles of this workgroup
+    const int ntm = (int)((g.M + 255) / 256), ntn = (int)((g.N + 255) / 256);
+    for (int t = blockIdx.x; t < ntm * ntn; t += gridDim.x) {
+        int tm, tn;
+        big_tile_coords(t, ntm, ntn, tm, tn);
+        big_tile<false, B2D, OUT, false, FQ_NONE>(g, tm, tn, smem);
+        __syncthreads();  // the next tile's copies overwrite the epilogue's staging
+    }
+}
+
+template <int IN, int RND, bool B2D, int OUT>
+static hipError_t launch_fused_a_k(const GemmArgs& g, const FusedA& f, hipStream_t s) {
+    using C = Big<false>;
+    auto k = k_gemm_fused_a<IN, RND, B2D, OUT>;
+    const size_t lds = (size_t)C::NST * C::STAGE;
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    int per_cu = 0, dev = 0, cus = 0;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, C::NTH, lds)) != hipSuccess) return e;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    const int64_t tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
+    const int64_t resident = (int64_t)per_cu * cus;
+    if (resident < 1) return hipErrorInvalidConfiguration;
+    const unsigned grid = (unsigned)(tiles < resident ? tiles : resident);
+    GemmArgs ga = g;
+    FusedA fa = f;
+    void* args[] = {&ga, &fa};
+    return hipLaunchCooperativeKernel((const void*)k, dim3(grid), dim3(C::NTH), args, (unsigned)lds, s);
+}
+
+hipError_t launch_gemm_fused_a(const GemmArgs& g, const SegArgs& a, int in_dtype, int hn, int rnd, int c_dtype,
+                               uint32_t* ws, hipStream_t s) {
+    FusedA f{};
+    f.a = a;
+    f.done = ws;
+    f.status = ws + 1;
+    f.units = (a.nseg + 63) / 64;
+    f.hn = hn;
+    hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(256), 0, s, ws, 2, 0u);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+#define BGF_FA(IN, RND)                                                                              \
+    do {                                                                                             \
+        if (g.b_2d) {                                                                                \
+            if (c_dtype == DT_BF16) return launch_fused_a_k<IN, RND, true, DT_BF16>(g, f, s);         \
+            return launch_fused_a_k<IN, RND, true, DT_F32>(g, f, s);                                  \
+        }                                                                                            \
+        if (c_dtype == DT_BF16) return launch_fused_a_k<IN, RND, false, DT_BF16>(g, f, s);            \
+        return launch_fused_a_k<IN, RND, false, DT_F32>(g, f, s);                                     \
+    } while (0)
+    if (in_dtype == DT_BF16) {
+        if (rnd == RND_SR) BGF_FA(DT_BF16, RND_SR);
+        BGF_FA(DT_BF16, RND_RNE);
+    }
+    if (rnd == RND_SR) BGF_FA(DT_F32, RND_SR);
+    BGF_FA(DT_F32, RND_RNE);
+#undef BGF_FA
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -727,27 +1084,8 @@ __global__ __launch_bounds__(256) void k_nv_to_fp8(NvPair pr) {
     uint8_t* const out_scales = op ? pr.out_scales[1] : pr.out_scales[0];
     const u32x4 q = *reinterpret_cast<const u32x4*>(codes + gi * 16);
     const uint32_t s01 = *reinterpret_cast<const uint16_t*>(scales + gi * 2);
-    const float s0 = e4m3_value(s01 & 0x7Fu), s1 = e4m3_value((s01 >> 8) & 0x7Fu);
-    const float S = fmaxf(s0, s1);
-    // E = smallest exponent with 448 * 2^E >= 6 S (6 S is exact in fp32)
-    const int E = e8m0_exp<8, 0x600000u>(6.0f * S, true);
-    out_scales[gi] = (uint8_t)(E + 127);
-    const uint32_t qw[4] = {q[0], q[1], q[2], q[3]};
     uint32_t o[8];
-    const float sc = E > -127 ? pow2f(E) : 1.0f;  // S = 0: every product is 0
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const float sb = w < 2 ? s0 : s1;
-        const v2f p0 = fp4x2_to_f32<0>(qw[w]), p1 = fp4x2_to_f32<1>(qw[w]);
-        const v2f p2 = fp4x2_to_f32<2>(qw[w]), p3 = fp4x2_to_f32<3>(qw[w]);
-        uint32_t r0 = 0u, r1 = 0u;
-        r0 = cvt_fp8x2<false>(r0, p0[0] * sb, p0[1] * sb, sc);
-        r0 = cvt_fp8x2<true>(r0, p1[0] * sb, p1[1] * sb, sc);
-        r1 = cvt_fp8x2<false>(r1, p2[0] * sb, p2[1] * sb, sc);
-        r1 = cvt_fp8x2<true>(r1, p3[0] * sb, p3[1] * sb, sc);
-        o[2 * w] = r0;
-        o[2 * w + 1] = r1;
-    }
+    out_scales[gi] = (uint8_t)nv_group_to_fp8(q, s01, o);
     u32x4* dst = reinterpret_cast<u32x4*>(out + gi * 32);
     dst[0] = (u32x4){o[0], o[1], o[2], o[3]};
     dst[1] = (u32x4){o[4], o[5], o[6], o[7]};
@@ -795,7 +1133,18 @@ static hipError_t launch_kind(const GemmArgs& g, int kind, int c_dtype, hipStrea
         return launch_out<false, false, false, FQ>(g, c_dtype, s);
     }
     if (kind == 1) return launch_out<true, false, false, FQ>(g, c_dtype, s);
-    // NVFP4: re-express both operands, then the FP8 product with the tensor scales
+    // NVFP4 with no workspace: the re-expression in LDS (256 x 256 tiles, any K % 128 == 0)
+    if (!g.a8 && g.M >= 256 && g.N >= 256 && g.M * (g.K / 2) < (1ll << 31) && g.N * (g.K / 2) < (1ll << 31)) {
+        const unsigned tiles = (unsigned)(((g.M + 255) / 256) * ((g.N + 255) / 256));
+        const size_t lds = (size_t)NvLds::LDS;
+        auto k = c_dtype == DT_BF16 ? k_gemm_nv<DT_BF16, FQ> : k_gemm_nv<DT_F32, FQ>;
+        hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k, dim3(tiles), dim3(512), lds, s, g);
+        return hipGetLastError();
+    }
+    if (!g.a8) return hipErrorInvalidValue;
+    // NVFP4: re-express both operands into the workspace, then the FP8 product with the tensor scales
     const int64_t ga = g.M * (g.K / 32), gb = g.N * (g.K / 32);
     NvPair pr{{g.a, g.b}, {g.sa, g.sb}, {g.a8, g.b8}, {g.sa8, g.sb8}, {ga, gb}};
     hipLaunchKernelGGL(k_nv_to_fp8, dim3((unsigned)((ga + gb + 255) / 256)), dim3(256), 0, s, pr);

@@ -88,6 +88,10 @@ def lib() -> ctypes.CDLL:
     L.fp4_gemm.restype = ctypes.c_int
     L.fp4_quantize_noalloc.argtypes = [P, I32, I64, I64, I64, QP, P, P, P, P]
     L.fp4_quantize_noalloc.restype = ctypes.c_int
+    L.fp4_gemm_quantize_a_workspace_bytes.argtypes = [I64, QT]
+    L.fp4_gemm_quantize_a_workspace_bytes.restype = I64
+    L.fp4_gemm_quantize_a.argtypes = [P, I32, I64, I64, QP, QT, QT, P, I32, I64, P, I64, P]
+    L.fp4_gemm_quantize_a.restype = ctypes.c_int
     L.fp4_transpose_2d.argtypes = [P, P, I64, I64, QP, P, P, P]
     L.fp4_transpose_2d.restype = ctypes.c_int
     L.fp4_nvfp4_to_mxfp8.argtypes = [P, P, I64, I64, P, P, P]
@@ -364,13 +368,14 @@ def gemm_workspace_bytes(a: QTensor, b: QTensor) -> int:
 
 def gemm(a: QTensor, b: QTensor, out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
          workspace: torch.Tensor | None = None, out_q: Params | None = None,
-         q_out: QTensor | None = None, keep_c: bool = True):
+         q_out: QTensor | None = None, keep_c: bool = True, use_workspace: bool = True):
     """C [M, N] = A [M, K] * B [N, K]^T on quantized operands (fp32 accumulation).
 
     With out_q (MX groups of 32 along N, E8M0 floor / ceil, RNE or SR, optionally rotated along N
     with out_q.hadamard_n <= 128), C is also quantized in the epilogue and (C, C_q) is returned;
     keep_c=False skips writing C and returns (None, C_q). out may be a column block of a wider
-    row-major buffer (its row pitch is passed as ldc)."""
+    row-major buffer (its row pitch is passed as ldc). use_workspace=False passes no workspace: NVFP4
+    operands (M, N >= 256) then take the route that re-expresses them as FP8 in LDS."""
     dev = a.codes.device
     if out is not None:
         if out.dim() != 2 or tuple(out.shape) != (a.rows, b.rows) or out.device != dev:
@@ -382,7 +387,9 @@ def gemm(a: QTensor, b: QTensor, out_dtype=torch.bfloat16, out: torch.Tensor | N
     c = None
     if out_q is None or keep_c:
         c = out if out is not None else torch.empty(a.rows, b.rows, dtype=out_dtype, device=dev)
-    wb = gemm_workspace_bytes(a, b)
+    wb = gemm_workspace_bytes(a, b) if use_workspace else 0
+    if not use_workspace:
+        workspace = None
     if wb and workspace is None:
         workspace = torch.empty(wb, dtype=torch.uint8, device=dev)
     ac, bc = a.c(), b.c()
@@ -439,6 +446,43 @@ def nvfp4_to_mxfp8(q: QTensor) -> QTensor:
                                   scales.data_ptr(), _stream_ptr(dev))
     _check(st, "fp4_nvfp4_to_mxfp8")
     return QTensor(codes, scales, q.tensor_scale, q.rows, q.cols, p8)
+
+
+def gemm_quantize_a(x: torch.Tensor, params: Params, b: QTensor, out_dtype=torch.bfloat16,
+                    out: torch.Tensor | None = None, a_out: QTensor | None = None,
+                    workspace: torch.Tensor | None = None):
+    """C = quantize(x) * B^T with x's rotation and MXFP4 quantization fused into the GEMM launch.
+    Returns (C, A_q), A_q the quantized x (the same codes and scales quantize() gives)."""
+    if x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D CUDA tensor, contiguous along its last axis")
+    dev = x.device
+    M, K = x.shape
+    if K != b.cols:
+        raise ValueError(f"x has {K} columns, B has {b.cols}")
+    _check_q(b, b.rows, b.cols, b.params, dev, "b")
+    if a_out is not None:
+        _check_q(a_out, M, K, params, dev, "a_out")
+    aq = a_out if a_out is not None else empty_qtensor(M, K, params, dev)
+    if out is not None:
+        if out.dim() != 2 or tuple(out.shape) != (M, b.rows) or out.device != dev or out.stride(1) != 1 \
+                or out.stride(0) < b.rows:
+            raise ValueError(f"out must be a row-major [{M}, {b.rows}] tensor on {dev}")
+    c = out if out is not None else torch.empty(M, b.rows, dtype=out_dtype, device=dev)
+    bc = b.c()
+    wb = lib().fp4_gemm_quantize_a_workspace_bytes(M, ctypes.byref(bc))
+    if wb < 0:
+        raise Fp4Error(ERR_INVALID_ARG, "fp4_gemm_quantize_a_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(wb, dtype=torch.uint8, device=dev)
+    wsb = _ws_bytes(workspace, wb, dev)
+    p = params.c()
+    ac = aq.c()
+    st = lib().fp4_gemm_quantize_a(x.data_ptr(), _dtype_code(x), M, x.stride(0), ctypes.byref(p), ctypes.byref(ac),
+                                   ctypes.byref(bc), c.data_ptr(), _dtype_code(c), c.stride(0),
+                                   workspace.data_ptr(), wsb, _stream_ptr(dev))
+    _check(st, "fp4_gemm_quantize_a")
+    aq.rows, aq.cols, aq.params, aq.tensor_scale = M, K, params, None
+    return c, aq
 
 
 def upload_qtensor(codes, scales, tensor_scale, rows, cols, params: Params, device) -> QTensor:

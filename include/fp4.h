@@ -226,6 +226,26 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
              const fp4_qparams* out_q, fp4_qtensor* C_q, void* workspace, int64_t ws_bytes,
              void* stream);
 
+/* The MXFP4 GEMM with A's rotation and quantization fused in ("fused rotation" before the 4-bit GEMM
+ * in the QuTLASS kernel list of the Quartet notes): a [M, K] (fp32 or bf16, row pitch lda) is rotated
+ * along K by H_n / sqrt(n) (n = pa->hadamard_n, which must equal B's) and quantized with *pa
+ * (E2M1, (1, 32) E8M0 floor or ceil, nearest even or stochastic; n in {0, 16, 32, 64, 128}), and
+ * C [M, N] = A_q B^T as fp4_gemm computes it (B: MXFP4, (1, 32) or (32, 32) blocks, K = B->cols).
+ * A_q->codes / A_q->scales (device, as fp4_quantize writes them) receive A's codes and scales, the
+ * same bytes fp4_quantize returns, and the product uses them; A_q->rows, cols, p, tensor_scale are
+ * set to M, K, *pa, NULL. On the 256 x 256 tile path (M, N >= 256, K % 256 == 0) one persistent
+ * launch first quantizes A with the whole grid (A once, not once per tile), then hands it over with
+ * one grid-wide release / acquire and runs the tiles (the workgroups must all be resident: the
+ * launch is cooperative, which fails with FP4_ERR_HIP when it cannot be); other shapes run the
+ * quantize launch and then fp4_gemm. workspace: fp4_gemm_quantize_a_workspace_bytes(M, B) bytes
+ * (256) of device memory: a counter and a status word, cleared by the call; the status word is
+ * non-zero afterwards only if the hand-over wait gave up (never with every workgroup resident). Requirements and alignment as for
+ * fp4_quantize (a, lda) and fp4_gemm (C, ldc); C is required. */
+int64_t fp4_gemm_quantize_a_workspace_bytes(int64_t M, const fp4_qtensor* B);
+int fp4_gemm_quantize_a(const void* a, int32_t a_dtype, int64_t M, int64_t lda, const fp4_qparams* pa,
+                        fp4_qtensor* A_q, const fp4_qtensor* B, void* C, int32_t c_dtype, int64_t ldc,
+                        void* workspace, int64_t ws_bytes, void* stream);
+
 /* The quantized form of the transpose of a tensor quantized with 32 x 32 blocks ((32, 32) E8M0 tiles,
  * E2M1 or E4M3 elements, hadamard_n == 0): codes / scales of T [rows, cols] become out_codes /
  * out_scales of T^T [cols, rows], exactly what fp4_quantize with the same *p returns for T^T (one

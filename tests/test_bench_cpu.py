@@ -138,3 +138,30 @@ def test_small_workloads_are_selectable():
         r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2", "--workload", name],
                            capture_output=True, text=True, timeout=120)
         assert r.returncode == 2 and "one GPU" in r.stderr  # parsed, then refused before any GPU work
+
+
+@pytest.mark.parametrize("name", sorted(bench.WORKLOADS))
+def test_workload_inputs_have_the_stated_shapes(name, monkeypatch):
+    """inputs_of returns A [M, K] and B as the step takes it ([N, K], or [K, N] when B is re-laid out
+    from its stored orientation, or [tokens, features] for the column-wise workload); generators are
+    replaced by shape-only stand-ins so that nothing large is drawn."""
+    wk = bench.WORKLOADS[name]
+    calls = {}
+
+    def fake(tag):
+        def f(seed, **kw):
+            calls[tag] = True
+            return tag
+        return f
+
+    import bit_gemm_fwht_amd.workloads as wlm
+    for tag in ("llama_linear", "backward_2d", "nvfp4_4over6", "backward_dw", "forward_2d"):
+        monkeypatch.setattr(wlm, tag, fake(tag))
+    want = {"llama7b": "llama_linear", "backward_2d": "backward_2d", "nvfp4": "nvfp4_4over6",
+            "backward_dw": "backward_dw", "forward_2d": "forward_2d"}
+    try:
+        bench.inputs_of(name)
+    except (TypeError, ValueError):
+        pass  # unpacking the stand-in fails after the generator was chosen
+    tag = next(v for k, v in want.items() if name.startswith(k))
+    assert calls == {tag: True}, (name, calls)

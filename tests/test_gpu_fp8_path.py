@@ -219,3 +219,50 @@ def test_mxfp4_products_are_summed_exactly():
     c = fp4.gemm(qa, qb, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert c[0, 0].item() == 36.0 + 36.0 + 6 * 0.25
+
+
+# ---------------------------------------------------------------------------------------------
+# NVFP4 x NVFP4 with the re-expression in LDS (no workspace)
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (300, 520, 384), (512, 768, 1024), (257, 511, 640)])
+def test_nvfp4_gemm_in_lds_equals_the_prepass_route(orc, M, N, K):
+    """The route without a workspace re-expresses the operands in LDS with the same arithmetic and
+    runs the same MFMA sequence: C is bit-identical to the pre-pass route (fp32 and bf16, with the
+    fused output quantize too), and meets the bound against the oracle."""
+    from test_gpu_parity import _gemm_check
+    rng = np.random.default_rng(M * 3 + N + K)
+    A = rng.laplace(size=(M, K)).astype(np.float32)
+    A.reshape(-1)[rng.choice(A.size, size=max(A.size // 1000, 1), replace=False)] *= 30
+    B = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    pa, pb = P(block=(1, 16), scale_mode=NV46), P(block=(1, 16), scale_mode=NV)
+    ca, sa, ta = _orc_quant(orc, A, pa)
+    cb, sb, tb = _orc_quant(orc, B, pb)
+    qa = fp4.upload_qtensor(ca, sa, ta, M, K, pa, DEV)
+    qb = fp4.upload_qtensor(cb, sb, tb, N, K, pb, DEV)
+    for dt in (torch.float32, torch.bfloat16):
+        c_ws = fp4.gemm(qa, qb, out_dtype=dt)
+        c_lds = fp4.gemm(qa, qb, out_dtype=dt, use_workspace=False)
+        torch.cuda.synchronize()
+        assert torch.equal(c_ws.view(torch.int16) if dt == torch.bfloat16 else c_ws.view(torch.int32),
+                           c_lds.view(torch.int16) if dt == torch.bfloat16 else c_lds.view(torch.int32))
+    oq = P(scale_mode=fp4.SCALE_E8M0_CEIL)
+    if N % 32 == 0:
+        c1, q1 = fp4.gemm(qa, qb, out_dtype=torch.float32, out_q=oq)
+        c2, q2 = fp4.gemm(qa, qb, out_dtype=torch.float32, out_q=oq, use_workspace=False)
+        torch.cuda.synchronize()
+        assert torch.equal(c1, c2) and torch.equal(q1.codes, q2.codes) and torch.equal(q1.scales, q2.scales)
+    _gemm_check(orc, A, B, pa, pb)  # and the pre-pass route against the oracle on the same operands
+
+
+def test_nvfp4_gemm_in_lds_full_size(orc):
+    """8192^3 NVFP4 + 4/6 (the benchmark's operands): the in-LDS route's C equals the pre-pass
+    route's bit for bit."""
+    from test_gpu_parity import _to_dev
+    x, w = wl.nvfp4_4over6(0)
+    p = P(block=(1, 16), scale_mode=NV46)
+    qx = fp4.quantize(_to_dev(x), p)
+    qw = fp4.quantize(_to_dev(w), p)
+    c1 = fp4.gemm(qx, qw, out_dtype=torch.bfloat16)
+    c2 = fp4.gemm(qx, qw, out_dtype=torch.bfloat16, use_workspace=False)
+    torch.cuda.synchronize()
+    assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
