@@ -157,6 +157,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-fraction", type=float, default=None,
                     help="fraction f of A rows and B rows the CPU oracle processes")
+    ap.add_argument("--k", type=int, default=0,
+                    help="headline workload only: another contraction depth K (a multiple of 256), e.g. a long K "
+                         "that amortises the GEMM's first round and epilogue over more main-loop stages")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
@@ -173,11 +176,12 @@ def params_of(fp4, spec):
                       hadamard_n=spec.get("hadamard_n", 0), seed=7 if spec.get("sr") else 0)
 
 
-def inputs_of(name):
-    """Host bf16 bit patterns (A, B) of a workload: A [M, K] is the left operand."""
+def inputs_of(name, k=0):
+    """Host bf16 bit patterns (A, B) of a workload: A [M, K] is the left operand (k: another K for
+    the headline workload)."""
     from bit_gemm_fwht_amd import workloads as wl
     if name == "llama7b_forward_linear":
-        x, w, _ = wl.llama_linear(0)
+        x, w, _ = wl.llama_linear(0, k=k) if k else wl.llama_linear(0)
         return x, w
     if name.startswith("backward_2d"):
         w, dy = wl.backward_2d(0)
@@ -598,10 +602,14 @@ def main():
     if args.workload == "mnist_mlp":
         return run_mnist(args)
     dev = torch.device("cuda:0")
-    wk = WORKLOADS[args.workload]
+    wk = dict(WORKLOADS[args.workload])
+    if args.k:
+        if args.workload != HEADLINE or args.k % 256:
+            raise SystemExit(f"--k applies to {HEADLINE} only and must be a multiple of 256")
+        wk["K"] = args.k
     M, N, K = wk["M"], wk["N"], wk["K"]
     pa, pb = params_of(fp4, wk["a"]), params_of(fp4, wk["b"])
-    a_bits, b_bits = inputs_of(args.workload)
+    a_bits, b_bits = inputs_of(args.workload, args.k)
     a0 = torch.from_numpy(a_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     b0 = torch.from_numpy(b_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     As = [a0] + [a0.clone() for _ in range(args.copies - 1)]
@@ -734,7 +742,7 @@ def main():
                    "input_copies": args.copies},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
-                     "traffic": measured_traffic() if args.workload == HEADLINE else None,
+                     "traffic": measured_traffic() if args.workload == HEADLINE and not args.k else None,
                      "kernel": wk["kernel"]},
         "quantize": {"GB/s": round(bytes_q / tq / 1e9, 1),
                      "frac": round(bytes_q / tq / 1e9 / HBM_PEAK_GBS, 4),

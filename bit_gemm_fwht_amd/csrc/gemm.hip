@@ -26,6 +26,7 @@
 // matrix core takes: per group, with S the larger of its two block scales, E is the smallest
 // exponent with 448 * 2^E >= 6 S and every element becomes E4M3(val(q) * s_blk * 2^-E) (nearest
 // even). The MXFP8 product is then scaled by RN(g_A * g_B) in the epilogue.
+#include <atomic>
 #include <type_traits>
 
 #include "device.h"
@@ -1011,12 +1012,26 @@ __global__ __launch_bounds__(512) void k_gemm_fused_a(GemmArgs g, FusedA f) {
     }
 }
 
+// Raises KERNEL's dynamic LDS limit to `lds` bytes once per device (the attribute belongs to the
+// function on the current device), instead of on every launch.
+template <auto KERNEL>
+static hipError_t allow_lds(size_t lds) {
+    static std::atomic<uint64_t> done{0};  // bit d: set on device d
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 64 && ((done.load(std::memory_order_acquire) >> dev) & 1u)) return hipSuccess;
+    e = hipFuncSetAttribute((const void*)KERNEL, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess && dev < 64) done.fetch_or(uint64_t(1) << dev, std::memory_order_acq_rel);
+    return e;
+}
+
 template <int IN, int RND, bool B2D, int OUT>
 static hipError_t launch_fused_a_k(const GemmArgs& g, const FusedA& f, hipStream_t s) {
     using C = Big<false>;
     auto k = k_gemm_fused_a<IN, RND, B2D, OUT>;
     const size_t lds = (size_t)C::NST * C::STAGE;
-    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = allow_lds<k_gemm_fused_a<IN, RND, B2D, OUT>>(lds);
     if (e != hipSuccess) return e;
     int per_cu = 0, dev = 0, cus = 0;
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, C::NTH, lds)) != hipSuccess) return e;
@@ -1108,15 +1123,13 @@ static hipError_t launch_out(const GemmArgs& g, int c_dtype, hipStream_t s) {
         const unsigned tiles = (unsigned)(((g.M + 255) / 256) * ((g.N + 255) / 256));
         const size_t lds = (size_t)C::NST * C::STAGE;
         if (c_dtype == DT_BF16) {
-            auto k = k_gemm_big<FP8, B2D, DT_BF16, NVG, FQ>;
-            hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            hipError_t e = allow_lds<k_gemm_big<FP8, B2D, DT_BF16, NVG, FQ>>(lds);
             if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(k, dim3(tiles), dim3(C::NTH), lds, s, g);
+            hipLaunchKernelGGL((k_gemm_big<FP8, B2D, DT_BF16, NVG, FQ>), dim3(tiles), dim3(C::NTH), lds, s, g);
         } else {
-            auto k = k_gemm_big<FP8, B2D, DT_F32, NVG, FQ>;
-            hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            hipError_t e = allow_lds<k_gemm_big<FP8, B2D, DT_F32, NVG, FQ>>(lds);
             if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(k, dim3(tiles), dim3(C::NTH), lds, s, g);
+            hipLaunchKernelGGL((k_gemm_big<FP8, B2D, DT_F32, NVG, FQ>), dim3(tiles), dim3(C::NTH), lds, s, g);
         }
         return hipGetLastError();
     }
@@ -1137,10 +1150,10 @@ static hipError_t launch_kind(const GemmArgs& g, int kind, int c_dtype, hipStrea
     if (!g.a8 && g.M >= 256 && g.N >= 256 && g.M * (g.K / 2) < (1ll << 31) && g.N * (g.K / 2) < (1ll << 31)) {
         const unsigned tiles = (unsigned)(((g.M + 255) / 256) * ((g.N + 255) / 256));
         const size_t lds = (size_t)NvLds::LDS;
-        auto k = c_dtype == DT_BF16 ? k_gemm_nv<DT_BF16, FQ> : k_gemm_nv<DT_F32, FQ>;
-        hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = c_dtype == DT_BF16 ? allow_lds<k_gemm_nv<DT_BF16, FQ>>(lds) : allow_lds<k_gemm_nv<DT_F32, FQ>>(lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k, dim3(tiles), dim3(512), lds, s, g);
+        if (c_dtype == DT_BF16) hipLaunchKernelGGL((k_gemm_nv<DT_BF16, FQ>), dim3(tiles), dim3(512), lds, s, g);
+        else hipLaunchKernelGGL((k_gemm_nv<DT_F32, FQ>), dim3(tiles), dim3(512), lds, s, g);
         return hipGetLastError();
     }
     if (!g.a8) return hipErrorInvalidValue;
