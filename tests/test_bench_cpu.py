@@ -165,3 +165,10 @@ def test_workload_inputs_have_the_stated_shapes(name, monkeypatch):
         pass  # unpacking the stand-in fails after the generator was chosen
     tag = next(v for k, v in want.items() if name.startswith(k))
     assert calls == {tag: True}, (name, calls)
+
+
+def test_event_stride_leaves_enough_samples():
+    import bench
+    for steps, stride in ((1, 1), (20, 1), (31, 1), (32, 2), (50, 3), (128, 8), (200, 8), (5000, 8)):
+        assert bench.event_stride(steps) == stride
+        assert len(range(0, steps, stride)) >= min(steps, 16)
