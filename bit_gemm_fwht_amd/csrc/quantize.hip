@@ -75,11 +75,59 @@ __device__ __forceinline__ void load_block_segments_t(const SegArgs& a, int64_t 
     }
 }
 
-// NVFP4 candidate: s = E4M3(amax_b / RN(M g)), d = RN(val(s) g)
-__device__ __forceinline__ uint32_t nv_candidate(float amax, float g, float M, float& d) {
-    const float t = amax / (M * g);
+// NVFP4 block scales of one tensor scale g: entry s of the table holds d = RN(val(s) g) and its
+// reciprocal RN(1/d) (0 for d = 0), so that a block needs no division for its reciprocal. Filled by
+// the workgroup's first 128 threads (code 0x7F, E4M3's NaN, is never chosen: the code saturates).
+__device__ __forceinline__ void nv_table_fill(float2* tab, float g) {
+    if (threadIdx.x < 128) {
+        const uint32_t s = threadIdx.x;
+        const float d = s < 0x7Fu ? e4m3_value(s) * g : 0.0f;
+        tab[s] = make_float2(d, scale_recip(d));
+    }
+}
+
+// The divisors of one tensor's block-scale quotients: c = RN(M g) for M = 6 and 4, their
+// reciprocals RN(1/c), and whether both c lie in [2^-100, 2^100] (then the quotients below need no
+// division).
+struct NvDiv {
+    float c6, y6, c4, y4;
+    bool fast;
+};
+__device__ __forceinline__ NvDiv nv_div(float g) {
+    NvDiv n;
+    n.c6 = 6.0f * g;
+    n.c4 = 4.0f * g;
+    n.y6 = 1.0f / n.c6;
+    n.y4 = 1.0f / n.c4;
+    n.fast = n.c6 >= 0x1p-100f && n.c6 <= 0x1p100f && n.c4 >= 0x1p-100f && n.c4 <= 0x1p100f;
+    return n;
+}
+
+// RN(a / c) from y = RN(1/c) with two Markstein corrections (Markstein, "Computation of elementary
+// functions on the IBM RISC System/6000 processor", 1990): q0 = RN(a y) is within 1.5 ulp of a/c,
+// q1 = RN(q0 + RN(a - c q0) y) within one ulp, and with r1 = a - c q1 exact (a fused multiply-add)
+// RN(q1 + r1 y) is the correctly rounded quotient. Valid while nothing underflows or overflows:
+// c and a (or a = 0) in [2^-100, 2^100], checked by the caller.
+__device__ __forceinline__ float div_by_recip(float a, float c, float y) {
+    const float q0 = a * y;
+    const float r0 = __builtin_fmaf(-c, q0, a);
+    const float q1 = __builtin_fmaf(r0, y, q0);
+    const float r1 = __builtin_fmaf(-c, q1, a);
+    return __builtin_fmaf(r1, y, q1);
+}
+
+// NVFP4 candidate: s = E4M3(amax_b / RN(M g)), d = RN(val(s) g), r = RN(1/d); c = RN(M g), y = RN(1/c)
+__device__ __forceinline__ uint32_t nv_candidate(float amax, float c, float y, bool fast, const float2* tab,
+                                                 float& d, float& r) {
+    float t;
+    if (fast && (amax == 0.0f || (amax >= 0x1p-100f && amax <= 0x1p100f)))
+        t = div_by_recip(amax, c, y);
+    else
+        t = amax / c;
     const uint32_t s = e4m3_code_sat(t);
-    d = e4m3_value(s) * g;
+    const float2 e = tab[s];
+    d = e.x;
+    r = e.y;
     return s;
 }
 
@@ -115,24 +163,24 @@ __device__ __forceinline__ float nv_codes_sse(const float (&v)[32], float d, flo
 // NVFP4 path for one 16-element block: returns the E4M3 scale code. With four_six (RNE only) both
 // candidates are encoded once; the SSE comparison picks one and its codes are kept as they are.
 template <int RND, int OFF>
-__device__ __forceinline__ uint32_t nv_block(float (&v)[32], float amax, float g, bool four_six,
-                                             const SrSource& sr, uint32_t (&out)[8]) {
-    float d;
-    uint32_t s = nv_candidate(amax, g, 6.0f, d);
+__device__ __forceinline__ uint32_t nv_block(float (&v)[32], float amax, const NvDiv& nd, const float2* tab,
+                                             bool four_six, const SrSource& sr, uint32_t (&out)[8]) {
+    float d, r;
+    uint32_t s = nv_candidate(amax, nd.c6, nd.y6, nd.fast, tab, d, r);
     if constexpr (RND == RND_RNE) {
         if (four_six) {
-            float d4;
-            const uint32_t s4 = nv_candidate(amax, g, 4.0f, d4);
+            float d4, r4;
+            const uint32_t s4 = nv_candidate(amax, nd.c4, nd.y4, nd.fast, tab, d4, r4);
             uint32_t c6[2], c4[2];
-            const float e6 = nv_codes_sse<OFF>(v, d, scale_recip(d), c6);
-            const float e4 = nv_codes_sse<OFF>(v, d4, scale_recip(d4), c4);
+            const float e6 = nv_codes_sse<OFF>(v, d, r, c6);
+            const float e4 = nv_codes_sse<OFF>(v, d4, r4, c4);
             const bool four = e4 < e6;
             out[OFF / 8] = four ? c4[0] : c6[0];
             out[OFF / 8 + 1] = four ? c4[1] : c6[1];
             return four ? s4 : s;
         }
     }
-    encode_block<ELEM_E2M1, RND, 16, OFF>(v, false, 1.0f, scale_recip(d), 448.0f, sr, out);
+    encode_block<ELEM_E2M1, RND, 16, OFF>(v, false, 1.0f, r, 448.0f, sr, out);
     return s;
 }
 
@@ -281,9 +329,13 @@ __global__ __launch_bounds__(kThreads) void k_segment(SegBatch b) {
                 g = amax_t > 0.0f ? amax_t / 2688.0f : 1.0f;
                 if (blk == 0 && threadIdx.x == 0) *a.tensor_scale = g;
             }
+            __shared__ float2 nvtab[128];
+            nv_table_fill(nvtab, g);
+            __syncthreads();
             const float m0 = block_amax<16, 0>(v), m1 = block_amax<16, 16>(v);
-            const uint32_t s0 = nv_block<RND, 0>(v, m0, g, a.four_six != 0, sr, out);
-            const uint32_t s1 = nv_block<RND, 16>(v, m1, g, a.four_six != 0, sr, out);
+            const NvDiv nd = nv_div(g);
+            const uint32_t s0 = nv_block<RND, 0>(v, m0, nd, nvtab, a.four_six != 0, sr, out);
+            const uint32_t s1 = nv_block<RND, 16>(v, m1, nd, nvtab, a.four_six != 0, sr, out);
             if (valid) reinterpret_cast<uint16_t*>(a.scales)[seg] = (uint16_t)(s0 | (s1 << 8));
         } else {  // SC_F32
             if constexpr (BC == 32) {

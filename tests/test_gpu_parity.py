@@ -644,3 +644,51 @@ def test_reused_outputs_describe_what_was_written(orc):
     assert cq2 is cq and cq.params == oq and (cq.rows, cq.cols) == (96, 64)
     oc, os_, _ = _orc_quant(orc, c.cpu().numpy(), oq)
     assert np.array_equal(cq.codes.cpu().numpy(), oc.reshape(-1))
+
+
+def _nv_quotient_edge_input(g, seed):
+    """fp32 [64, 512] whose 16-blocks have maxima spread over fp32's range (zeros included) and,
+    in half the rows, maxima placed at and one ulp around RN(mid * c) for E4M3 rounding midpoints
+    mid and c = RN(6 g), where the block-scale quotient amax / c lands on or next to a tie."""
+    rng = np.random.default_rng(seed)
+    x = rng.uniform(-1.0, 1.0, size=(64, 512)).astype(np.float32)
+    blocks = x.reshape(-1, 16)
+    nb = blocks.shape[0]
+    mag = np.float32(2.0) ** rng.integers(-126, 120, size=nb).astype(np.float32)
+    blocks *= mag[:, None]
+    blocks[rng.choice(nb, size=nb // 16, replace=False)] = 0.0
+    c = np.float32(np.float32(6.0) * np.float32(g))
+    # E4M3 rounding midpoints between consecutive normal codes (1 + (2m + 1)/16) * 2^e
+    mids = np.array([(1 + (2 * m + 1) / 16) * 2.0 ** e for e in range(-6, 9) for m in range(8)], dtype=np.float32)
+    half = nb // 2
+    with np.errstate(over="ignore", under="ignore"):
+        target = (mids[rng.integers(0, mids.size, size=half)] * c).astype(np.float32)
+    step = rng.integers(-1, 2, size=half)
+    target = np.where(step < 0, np.nextafter(target, np.float32(0)),
+                      np.where(step > 0, np.nextafter(target, np.float32(np.inf)), target)).astype(np.float32)
+    ok = np.isfinite(target) & (target > 0)
+    tb = (rng.uniform(-0.5, 0.5, size=(int(ok.sum()), 16)) * target[ok][:, None].astype(np.float64)).astype(np.float32)
+    tb[:, 3] = target[ok]
+    blocks[half:][ok] = tb
+    assert np.isfinite(x).all()
+    return x
+
+
+@pytest.mark.parametrize("mode", [NVG, NV46G])
+@pytest.mark.parametrize("g", [2.0 ** -130, 2.0 ** -102, 2.0 ** -98, 1e-20, 3.1e-3, 1.0, 3.3e4, 2.0 ** 97, 2.0 ** 99, 2.0 ** 110])
+def test_nvfp4_block_scale_quotient_edges(orc, mode, g):
+    """The block-scale quotient amax / RN(M g) is computed from RN(1/RN(M g)) with two Markstein
+    corrections where divisor and block max lie in [2^-100, 2^100], and by division elsewhere:
+    codes and scales stay byte-exact against the oracle for tensor scales on both sides of those
+    bounds, block maxima across fp32's range, and maxima that put the quotient on or one ulp from an
+    E4M3 rounding midpoint."""
+    x = _nv_quotient_edge_input(g, seed=int(abs(np.log2(g))) + (mode == NV46G))
+    params = P(block=(1, 16), scale_mode=mode)
+    q = fp4.quantize(_to_dev(x), params, tensor_scale=float(np.float32(g)))
+    torch.cuda.synchronize()
+    oc, os_, _ = orc.quantize(x, block=(1, 16), scale_mode=mode, tensor_scale=float(np.float32(g)))
+    gc, gs = q.codes.cpu().numpy(), q.scales.cpu().numpy()
+    bad = np.nonzero(gs != os_.reshape(-1).view(np.uint8))[0]
+    assert bad.size == 0, f"{bad.size} scale bytes differ, first at {bad[:8]}"
+    bad = np.nonzero(gc != oc.reshape(-1))[0]
+    assert bad.size == 0, f"{bad.size} code bytes differ, first at {bad[:8]}"
