@@ -161,34 +161,40 @@ __device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32
 // p = (|v| - lo) / (hi - lo) (exact: the gap is a power of two). Saturates at the grid maximum.
 // Returns the code (sign bit 3 for E2M1, bit 7 for E4M3).
 // ---------------------------------------------------------------------------------------------
-// Both are branch-free: every lane evaluates the same instructions (the data-dependent branches of
-// a per-range formulation diverge within a wave on any real tensor).
+// Both are branch-free and select-free: |v| is clamped to the grid maximum (which then rounds to
+// the top code and never up), scaled by the grid spacing of its binade (a power of two, exact) to a
+// position q in grid steps, and lo's code follows from floor(q) and the binade's exponent field;
+// data-dependent branches per range would diverge within a wave on any real tensor.
 __device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t u16) {
-    const float a = fabsf(v);
-    // grid spacing 2^(e-1): e = 0 on [0, 2) (0, 0.5, 1, 1.5), 1 on [2, 4) (2, 3), 2 from 4 (4, 6)
-    const int e = min(max((int)(__float_as_uint(a) >> 23) - 127, 0), 2);
-    const float q = a * __uint_as_float((uint32_t)(128 - e) << 23);  // |v| in grid steps, exact
-    const float fl = floorf(q);                                      // lo's position (exact)
-    const float p = q - fl;                                          // exact, in [0, 1)
-    const uint32_t up = ((float)u16 < p * 65536.0f) ? 1u : 0u;
-    // codes: position fl on [0, 2) is code fl; on [2, 4) and [4, 6) code fl + 2 e
-    const uint32_t code = a < 6.0f ? (uint32_t)fl + 2u * (uint32_t)e + up : 7u;
+    // |v| clamped to 6 (a NaN clamps to 6 as well): the steps below then give code 7 and never
+    // round up, so saturation needs no select
+    const float a = fminf(fabsf(v), 6.0f);
+    const uint32_t ua = __float_as_uint(a);
+    // grid spacing 2^(e-1): e = 0 on [0, 2) (0, 0.5, 1, 1.5), 1 on [2, 4) (2, 3), 2 from 4 (4, 6);
+    // ue = the exponent field clamped to [127, 129] (e + 127)
+    const uint32_t ue = min(max(ua & 0x7F800000u, 0x3F800000u), 0x40800000u);
+    const float q = a * __uint_as_float(0x7F800000u - ue);  // |v| / 2^(e-1): position in grid steps, exact
+    const float fl = floorf(q);                             // lo's position (exact)
+    // up iff u16 < (q - fl) 2^16, i.e. fl + u16 2^-16 < q (both sides exact)
+    const uint32_t up = __builtin_fmaf((float)u16, 0x1p-16f, fl) < q ? 1u : 0u;
+    // codes: position fl on [0, 2) is code fl; on [2, 4) and [4, 6] code fl + 2 e
+    const uint32_t code = (uint32_t)(int)fl + (ue >> 22) - 254u + up;
     return ((__float_as_uint(v) >> 28) & 8u) | code;
 }
 
 __device__ __forceinline__ uint32_t e4m3_sr(float v, uint32_t u16) {
-    const float a = fabsf(v);
+    // |v| clamped to 448 (a NaN clamps to 448 as well): code 0x7E, never rounded up
+    const float a = fminf(fabsf(v), 448.0f);
     const uint32_t ua = __float_as_uint(a);
-    // normal E4M3 range (a >= 2^-6): 3 mantissa bits kept, lo = (biased e - 120) << 3 | top 3
-    // bits, and p * 2^16 is the 20 bits below them over 2^4 (an exact integer compare)
-    const uint32_t lo_n = (ua >> 20) - 960u;
-    const uint32_t up_n = (u16 << 4) < (ua & 0xFFFFFu) ? 1u : 0u;
-    // subnormal E4M3 (a < 2^-6): step 2^-9
-    const float s = a * 512.0f;
-    const float q = floorf(s);
-    const uint32_t up_s = ((float)u16 < (s - q) * 65536.0f) ? 1u : 0u;
-    uint32_t code = a >= 0.015625f ? lo_n + up_n : (uint32_t)q + up_s;
-    code = a < 448.0f ? code : 0x7Eu;
+    // grid spacing 2^(e-3) with e = max(exponent, -6) (subnormals share 2^-6's spacing 2^-9);
+    // ue = that exponent's field
+    const uint32_t ue = max(ua & 0x7F800000u, 0x3C800000u);
+    const float q = a * __uint_as_float(0x80800000u - ue);  // |v| / 2^(e-3): position in grid steps, exact
+    const float fl = floorf(q);                             // lo's position (exact)
+    // up iff u16 < (q - fl) 2^16, i.e. fl + u16 2^-16 < q (both sides exact)
+    const uint32_t up = __builtin_fmaf((float)u16, 0x1p-16f, fl) < q ? 1u : 0u;
+    // code 8 (e + 6) + fl: fl in [8, 16) for normals, [0, 8) below 2^-6
+    const uint32_t code = (uint32_t)(int)fl + (ue >> 20) - 968u + up;
     return ((__float_as_uint(v) >> 24) & 0x80u) | code;
 }
 
