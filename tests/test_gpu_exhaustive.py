@@ -5,6 +5,8 @@
   beside a 4.0 that fixes the group's floor-rule scale to 2^0, against the oracle's quantize.
 - E4M3 round-to-nearest-even (the scaled FP8 convert): every pattern with |v| < 512 beside a 256.0
   (scale 2^0 for E4M3's floor rule; (448, 512) saturates), against the oracle.
+- stochastic rounding to E2M1 and to E4M3 over the same two sweeps, with the same group scale pins,
+  against the oracle's rule fed the same Philox uniforms (element index within the launch).
 - fp32 -> bf16 (the hardware packed convert every bf16 output uses): dequantize with fp32 block
   scales d and unit codes returns bf16(1.0 * d) = bf16(d) for every fp32 pattern d, against torch's
   cast of d (the cast the oracle's bf16 rounding is pinned to).
@@ -42,10 +44,23 @@ def _oracle_quantize(orc, x, elem, threads=16):
     return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
 
 
-def _sweep(orc, elem, pin, npos):
+def _oracle_sr_codes(orc, x, elem, seed, threads=16):
+    """The oracle's stochastic rounding of x (a [rows, 32] chunk whose group scales are all 2^0, so
+    the elements are the values rounded) with element i of the chunk keyed by index i, packed as
+    the library packs codes; row slices in parallel, each with its own first index."""
+    flat = x.reshape(-1)
+    step = -(-flat.size // threads) // 32 * 32 + 32
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        parts = list(ex.map(lambda lo: orc.encode(flat[lo:lo + step], elem=elem, round_mode=orc.ROUND_SR,
+                                                   seed=seed, idx0=lo), range(0, flat.size, step)))
+    c = np.concatenate(parts)
+    return (c[0::2] | (c[1::2] << 4)).astype(np.uint8) if elem == fp4.E2M1 else c
+
+
+def _sweep(orc, elem, pin, npos, sr_seed=None):
     total = 2 * npos
     groups = -(-total // 31)
-    p = fp4.Params(elem=elem)
+    p = fp4.Params(elem=elem) if sr_seed is None else fp4.Params(elem=elem, round_mode=fp4.ROUND_SR, seed=sr_seed)
     done = 0
     for g0 in range(0, groups, ROWS):
         rows = min(ROWS, groups - g0)
@@ -56,8 +71,11 @@ def _sweep(orc, elem, pin, npos):
         torch.cuda.synchronize()
         codes, scales = q.codes.cpu().numpy(), q.scales.cpu().numpy()
         assert np.all(scales == 127), "the pinned group max must give the scale 2^0"
-        oc, os_ = _oracle_quantize(orc, x, elem)
-        assert np.array_equal(scales, os_.reshape(-1))
+        if sr_seed is None:
+            oc, os_ = _oracle_quantize(orc, x, elem)
+            assert np.array_equal(scales, os_.reshape(-1))
+        else:
+            oc = _oracle_sr_codes(orc, x, elem, sr_seed)
         bad = np.nonzero(codes != oc.reshape(-1))[0]
         assert bad.size == 0, f"{bad.size} code bytes differ in groups {g0}..{g0 + rows}, first byte {bad[0]}"
         done += rows
@@ -72,6 +90,18 @@ def test_e2m1_rne_every_fp32_below_8(orc):
 @pytest.mark.timeout(900)
 def test_e4m3_rne_every_fp32_below_512(orc):
     _sweep(orc, fp4.E4M3, 256.0, 0x44000000)  # 0x44000000 = 512.0
+
+
+@pytest.mark.timeout(900)
+def test_e2m1_sr_every_fp32_below_8(orc):
+    """Stochastic rounding to E2M1 (Philox4x32-10 16-bit uniforms keyed by element index) on every
+    fp32 pattern with |v| < 8, against the oracle's rule with the same uniforms."""
+    _sweep(orc, fp4.E2M1, 4.0, 0x41000000, sr_seed=0x5EED)
+
+
+@pytest.mark.timeout(900)
+def test_e4m3_sr_every_fp32_below_512(orc):
+    _sweep(orc, fp4.E4M3, 256.0, 0x44000000, sr_seed=0x5EED)
 
 
 @pytest.mark.timeout(900)
