@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-@pytest.mark.parametrize("rows,cols", [(64, 64), (96, 160), (256, 512), (32, 32), (4096, 4096)])
+@pytest.mark.parametrize("rows,cols", [(64, 64), (96, 160), (256, 512), (32, 32), (160, 288), (416, 96), (4096, 4096)])
 @pytest.mark.parametrize("elem,sm", [(fp4.E2M1, CEIL), (fp4.E2M1, FLOOR), (E4M3, CEIL)])
 def test_transpose_equals_quantize_of_transpose(orc, rows, cols, elem, sm):
     rng = np.random.default_rng(rows + cols + elem)
