@@ -450,7 +450,7 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
         if ((rc = check_operand(B)) != FP4_OK) return rc;
         if (A->cols != B->cols) return FP4_ERR_INVALID_ARG;
         const int64_t M = A->rows, N = B->rows, K = A->cols;
-        if (K % 128) return FP4_ERR_UNSUPPORTED;
+        if (K % 32) return FP4_ERR_INVALID_ARG;  // operand checks already keep K a multiple of 32
         if (A->p.hadamard_n != B->p.hadamard_n) return FP4_ERR_INVALID_ARG;
         int b2d;
         const int kind = gemm_kind(A, B, &b2d);
@@ -482,7 +482,7 @@ int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtyp
         }
         int64_t need = gemm_ws(A, B, kind);
         // NVFP4 without a workspace: the FP8 re-expression happens in LDS (256 x 256 tile shapes)
-        const bool nv_in_lds = kind == 2 && !workspace && ws_bytes == 0 && M >= 256 && N >= 256 &&
+        const bool nv_in_lds = kind == 2 && !workspace && ws_bytes == 0 && M >= 256 && N >= 256 && K % 128 == 0 &&
                                M * (K / 2) < (int64_t(1) << 31) && N * (K / 2) < (int64_t(1) << 31);
         if (nv_in_lds) need = 0;
         if (need && (!workspace || ws_bytes < need)) return FP4_ERR_WORKSPACE;
@@ -569,7 +569,6 @@ int fp4_gemm_quantize_a(const void* a, int32_t a_dtype, int64_t M, int64_t lda, 
         Aq.p = *pa;
         int b2d;
         if (gemm_kind(&Aq, B, &b2d) != 0) return FP4_ERR_UNSUPPORTED;  // B must be MXFP4 (1 x 32 or 2D)
-        if (K % 128) return FP4_ERR_UNSUPPORTED;
         const int64_t need = fp4_gemm_quantize_a_workspace_bytes(M, B);
         if (!workspace || ws_bytes < need) return FP4_ERR_WORKSPACE;
         if (!aligned(workspace, 4)) return FP4_ERR_ALIGNMENT;

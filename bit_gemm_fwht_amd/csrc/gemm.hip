@@ -5,7 +5,7 @@
 // tile). The matrix core applies both scales itself, so the main loop is loads + MFMA only.
 // Two kernels: k_gemm_big (256 x 256 tiles, 32x32x64 MFMA, operands copied straight into LDS; the
 // path for M, N >= 256 and K a multiple of its stage depth) and k_gemm below (128 x 128 tiles,
-// 16x16x128 MFMA; every other shape).
+// 16x16x128 MFMA; every other shape, K any multiple of 32).
 //
 // Lane layouts of the 16x16x128 scaled MFMA (established with one-hot probes on the hardware):
 //  - FP4: lane l supplies row l % 16 and the 32 K values [32 (l / 16), +32) as 16 contiguous
@@ -49,8 +49,22 @@ struct Cfg {
     static constexpr int LOADS = BM * CH / NT;     // 16-byte loads per thread per operand
 };
 
+// The four E8M0 scale bytes of K groups 4 kt .. 4 kt + 3 in one row of a scale matrix with kgroups
+// columns: one dword load when kgroups % 4 == 0 (the row starts stay 4-byte aligned), else single
+// bytes, with groups past the row as code 0 (their elements are zero, so the products are too).
+__device__ __forceinline__ uint32_t scale_dword(const uint8_t* row, int64_t kgroups, int kt) {
+    const int64_t g0 = 4 * (int64_t)kt;
+    if (!(kgroups & 3)) return *reinterpret_cast<const uint32_t*>(row + g0);
+    uint32_t v = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (g0 + j < kgroups) v |= (uint32_t)row[g0 + j] << (8 * j);
+    return v;
+}
+
 // One K step's global loads of the 128 x 128 kernel: LOADS 16-byte pieces of A and of B per
-// thread (rows beyond M / N read as zero) and one scale dword (threads < 128: A's rows, else B's).
+// thread (rows beyond M / N and pieces beyond K read as zero: K % 32 == 0 keeps each piece wholly
+// inside or outside a row) and one scale dword (threads < 128: A's rows, else B's).
 template <bool FP8, bool B2D>
 __device__ __forceinline__ void small_gload(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb,
                                             int64_t M, int64_t N, int64_t m0, int64_t n0, int64_t rowbytes,
@@ -62,16 +76,17 @@ __device__ __forceinline__ void small_gload(const uint8_t* a, const uint8_t* b, 
         const int ch = tid + NT * i, r = ch / C::CH, c = ch % C::CH;
         const int64_t m = m0 + r, n = n0 + r;
         const int64_t off = (int64_t)kt * C::RB + 16 * c;
-        ra[i] = m < M ? *reinterpret_cast<const u32x4*>(a + m * rowbytes + off) : (u32x4){0u, 0u, 0u, 0u};
-        rb[i] = n < N ? *reinterpret_cast<const u32x4*>(b + n * rowbytes + off) : (u32x4){0u, 0u, 0u, 0u};
+        const bool kin = off < rowbytes;
+        ra[i] = m < M && kin ? *reinterpret_cast<const u32x4*>(a + m * rowbytes + off) : (u32x4){0u, 0u, 0u, 0u};
+        rb[i] = n < N && kin ? *reinterpret_cast<const u32x4*>(b + n * rowbytes + off) : (u32x4){0u, 0u, 0u, 0u};
     }
     if (tid < BM) {
         const int64_t m = m0 + tid;
-        rsa = m < M ? *reinterpret_cast<const uint32_t*>(sa + m * kgroups + 4 * kt) : 0u;
+        rsa = m < M ? scale_dword(sa + m * kgroups, kgroups, kt) : 0u;
     } else {
         const int64_t n = n0 + (tid - BM);
         const int64_t srow = B2D ? (n >> 5) : n;
-        rsb = n < N ? *reinterpret_cast<const uint32_t*>(sb + srow * kgroups + 4 * kt) : 0u;
+        rsb = n < N ? scale_dword(sb + srow * kgroups, kgroups, kt) : 0u;
     }
 }
 
@@ -103,7 +118,7 @@ __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
     const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
     const int64_t rowbytes = FP8 ? g.K : g.K / 2;
     const int64_t kgroups = g.K / 32;
-    const int KT = (int)(g.K / BK);
+    const int KT = (int)((g.K + BK - 1) / BK);  // the last step may be partly past K
 
     u32x4 ra[C::LOADS], rb[C::LOADS];
     uint32_t rsa = 0, rsb = 0;
@@ -1146,8 +1161,8 @@ static hipError_t launch_kind(const GemmArgs& g, int kind, int c_dtype, hipStrea
         return launch_out<false, false, false, FQ>(g, c_dtype, s);
     }
     if (kind == 1) return launch_out<true, false, false, FQ>(g, c_dtype, s);
-    // NVFP4 with no workspace: the re-expression in LDS (256 x 256 tiles, any K % 128 == 0)
-    if (!g.a8 && g.M >= 256 && g.N >= 256 && g.M * (g.K / 2) < (1ll << 31) && g.N * (g.K / 2) < (1ll << 31)) {
+    // NVFP4 with no workspace: the re-expression in LDS (256 x 256 tiles, K % 128 == 0)
+    if (!g.a8 && g.M >= 256 && g.N >= 256 && g.K % Big<true>::KSTEP == 0 && g.M * (g.K / 2) < (1ll << 31) && g.N * (g.K / 2) < (1ll << 31)) {
         const unsigned tiles = (unsigned)(((g.M + 255) / 256) * ((g.N + 255) / 256));
         const size_t lds = (size_t)NvLds::LDS;
         hipError_t e = c_dtype == DT_BF16 ? allow_lds<k_gemm_nv<DT_BF16, FQ>>(lds) : allow_lds<k_gemm_nv<DT_F32, FQ>>(lds);

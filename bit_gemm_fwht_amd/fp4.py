@@ -375,7 +375,7 @@ def gemm(a: QTensor, b: QTensor, out_dtype=torch.bfloat16, out: torch.Tensor | N
     with out_q.hadamard_n <= 128), C is also quantized in the epilogue and (C, C_q) is returned;
     keep_c=False skips writing C and returns (None, C_q). out may be a column block of a wider
     row-major buffer (its row pitch is passed as ldc). use_workspace=False passes no workspace: NVFP4
-    operands (M, N >= 256) then take the route that re-expresses them as FP8 in LDS."""
+    operands (M, N >= 256, K % 128 == 0) then take the route that re-expresses them as FP8 in LDS."""
     dev = a.codes.device
     if out is not None:
         if out.dim() != 2 or tuple(out.shape) != (a.rows, b.rows) or out.device != dev:

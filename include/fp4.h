@@ -208,7 +208,10 @@ int fp4_hadamard(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int
  * E8M0 (1, 32)), and NVFP4 x NVFP4 (E2M1, (1, 16) NV or 4/6 scales: each 32-wide K group is
  * re-expressed as E4M3 elements under one power-of-two scale and multiplied on the FP8 matrix
  * cores, and the product of the two tensor scales is applied in the epilogue).
- * K % 128 == 0. Operands must not be rotated differently: a rotation along K cancels in A B^T
+ * K is a multiple of 32 (every operand layout requires it). The 256 x 256 tile kernels take
+ * M, N >= 256 and K % 256 == 0 (MXFP4) or K % 128 == 0 (MXFP8, NVFP4); every other shape runs on
+ * the 128 x 128 kernel, whose last 128-deep step may lie partly past K (it reads nothing there).
+ * Operands must not be rotated differently: a rotation along K cancels in A B^T
  * only when both were rotated with the same n, which the caller ensures.
  * Optional fused output quantization ("online quantization" of the output in the QuTLASS kernel
  * list of the Quartet notes): if out_q is non-NULL, C_q->codes / C_q->scales (device, codes
@@ -220,7 +223,9 @@ int fp4_hadamard(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int
  * unrotated). Requires N % 32 == 0 and N % n == 0 (n = 256: FP4_ERR_UNSUPPORTED);
  * C_q->rows, cols, p are set to M, N, *out_q and tensor_scale to
  * NULL. C may then be NULL (only the quantized output is written); out_q and C_q are given
- * together or not at all. workspace: fp4_gemm_workspace_bytes() bytes. */
+ * together or not at all. workspace: fp4_gemm_workspace_bytes() bytes; NVFP4 operands with
+ * M, N >= 256 and K % 128 == 0 may instead pass NULL and 0 (the re-expression then happens in LDS,
+ * inside the 256 x 256 tiles), other NVFP4 shapes return FP4_ERR_WORKSPACE without it. */
 int64_t fp4_gemm_workspace_bytes(const fp4_qtensor* A, const fp4_qtensor* B);
 int fp4_gemm(const fp4_qtensor* A, const fp4_qtensor* B, void* C, int32_t c_dtype, int64_t ldc,
              const fp4_qparams* out_q, fp4_qtensor* C_q, void* workspace, int64_t ws_bytes,

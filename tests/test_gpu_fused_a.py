@@ -66,6 +66,8 @@ CASES = [
     (1280, 256, 768, "f32", P(hadamard_n=64), P(hadamard_n=64), torch.float32),
     (128, 256, 256, "bf16", P(hadamard_n=128), P(hadamard_n=128), torch.float32),   # two-launch route: M < 256
     (512, 512, 384, "bf16", P(hadamard_n=128), P(hadamard_n=128), torch.bfloat16),  # two-launch route: K % 256
+    (300, 288, 224, "f32", P(hadamard_n=32), P(hadamard_n=32), torch.float32),      # two-launch route: K % 128
+    (64, 96, 96, "bf16", P(scale_mode=CEIL), P(block=(32, 32), scale_mode=CEIL), torch.bfloat16),
 ]
 
 

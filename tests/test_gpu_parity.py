@@ -321,6 +321,43 @@ def test_gemm_shapes(orc, M, N, K, kind):
     _gemm_check(orc, A, B, pa, pb, c_dtype=torch.bfloat16)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (200, 136, 96), (129, 256, 160), (300, 520, 224),
+                                   (257, 320, 4192)])
+@pytest.mark.parametrize("kind", ["mxfp4", "mxfp4_2d", "mxfp8", "nvfp4"])
+def test_gemm_k_not_a_multiple_of_128(orc, M, N, K, kind):
+    """K % 32 == 0 but K % 128 != 0: the last 128-deep step of the 128 x 128 kernel reads past K,
+    where the pieces of A and B are zero and the scale bytes of the missing groups code 0, so C is
+    the product over the real K (the same bound as every other shape)."""
+    rng = np.random.default_rng(M + 5 * N + K)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    if kind == "mxfp4":
+        pa, pb = P(), P(scale_mode=CEIL)
+    elif kind == "mxfp4_2d":
+        if N % 32:
+            pytest.skip("2D tiles need N % 32 == 0")
+        pa, pb = P(), P(block=(32, 32), scale_mode=CEIL)
+    elif kind == "mxfp8":
+        pa, pb = P(elem=E4M3), P(elem=E4M3, scale_mode=CEIL)
+    else:
+        pa, pb = P(block=(1, 16), scale_mode=NV46), P(block=(1, 16), scale_mode=NV)
+    _gemm_check(orc, A, B, pa, pb)
+    _gemm_check(orc, A, B, pa, pb, c_dtype=torch.bfloat16)
+
+
+def test_nvfp4_gemm_without_workspace_needs_k_multiple_of_128():
+    """The in-LDS re-expression runs 128-deep stages: with K % 128 != 0 an NVFP4 product needs the
+    workspace, and the call says so before it launches anything."""
+    M, N, K = 256, 256, 160
+    rng = np.random.default_rng(11)
+    pa = P(block=(1, 16), scale_mode=NV46)
+    qa = fp4.quantize(_to_dev(rng.standard_normal((M, K)).astype(np.float32)), pa)
+    qb = fp4.quantize(_to_dev(rng.standard_normal((N, K)).astype(np.float32)), pa)
+    with pytest.raises(fp4.Fp4Error) as ei:
+        fp4.gemm(qa, qb, use_workspace=False)
+    assert ei.value.status == fp4.ERR_WORKSPACE
+
+
 OUTQ_CASES = [(E2M1, FLOOR, RNE), (E2M1, CEIL, SR), (E4M3, FLOOR, RNE), (E4M3, CEIL, SR)]
 
 
