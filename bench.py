@@ -50,7 +50,8 @@ the summary's kernel source hash matches the current source. `cpu_baseline` time
 a bounded sample of the same step, at one thread and at every host thread the process may use (up
 to 16), and adds the CPU model and an fp32 torch.matmul on the host as a BLAS reference point.
 
-`--copy-calibration MIB` instead runs only a plain device-to-device copy of MIB MiB a few times
+`--shard S` measures one GPU's share of a column-parallel split over S GPUs (W's first N/S rows, all
+of X) at its real shape. `--copy-calibration MIB` instead runs only a plain device-to-device copy of MIB MiB a few times
 (the reference kernel whose FETCH_SIZE / WRITE_SIZE counter readings calibrate the GEMM's).
 """
 from __future__ import annotations
@@ -72,6 +73,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 GEMM_SRC = os.path.join(ROOT, "bit_gemm_fwht_amd", "csrc", "gemm.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_llama7b_forward_linear_traffic.md")
 HEADLINE = "llama7b_forward_linear"
+# workloads whose B is not a plain [N, K] row block (a stored W [K, N] re-laid out; column-wise operands)
+SHARD_EXCLUDED = {"forward_2d_transposed", "backward_dw_colwise"}
 
 # name -> shapes (C = A B^T: A [M, K], B [N, K]), quantization of A and B, CPU-sample fraction
 WORKLOADS = {
@@ -160,6 +163,10 @@ def parse():
     ap.add_argument("--k", type=int, default=0,
                     help="headline workload only: another contraction depth K (a multiple of 256), e.g. a long K "
                          "that amortises the GEMM's first round and epilogue over more main-loop stages")
+    ap.add_argument("--shard", type=int, default=1, metavar="S",
+                    help="one GPU's share of a column-parallel split over S GPUs: the GEMM over the first "
+                         "N/S rows of B (output features), all of A (A's quantize included, as each GPU "
+                         "would run it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
@@ -640,9 +647,17 @@ def main():
         if args.workload != HEADLINE or args.k % 256:
             raise SystemExit(f"--k applies to {HEADLINE} only and must be a multiple of 256")
         wk["K"] = args.k
+    if args.shard != 1:
+        n_s = wk["N"] // args.shard if args.shard > 1 else 0
+        if (args.workload in SHARD_EXCLUDED or n_s == 0 or wk["N"] % args.shard or n_s % 32):
+            raise SystemExit(f"--shard {args.shard}: not a column-parallel split of {args.workload} "
+                             f"(N = {wk['N']} must split into multiples of 32; not for {sorted(SHARD_EXCLUDED)})")
+        wk["N"] = n_s
     M, N, K = wk["M"], wk["N"], wk["K"]
     pa, pb = params_of(fp4, wk["a"]), params_of(fp4, wk["b"])
     a_bits, b_bits = inputs_of(args.workload, args.k)
+    if args.shard > 1:  # this GPU's rows of B: the first N/S output features
+        b_bits = np.ascontiguousarray(b_bits[:N])
     a0 = torch.from_numpy(a_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     b0 = torch.from_numpy(b_bits.view(np.int16)).to(dev).view(torch.bfloat16)
     As = [a0] + [a0.clone() for _ in range(args.copies - 1)]
@@ -776,10 +791,12 @@ def main():
         "data": "synthetic (seeded numpy draws of the workload's shapes and distributions)",
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "input": "bf16",
                    "hadamard_n": pa.hadamard_n, "quant": wk["quant"], "output": "bf16",
-                   "input_copies": args.copies},
+                   "input_copies": args.copies,
+                   **({"shard": f"1/{args.shard} of N (column-parallel; all of A)"} if args.shard > 1 else {})},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
-                     "traffic": measured_traffic() if args.workload == HEADLINE and not args.k else None,
+                     "traffic": (measured_traffic() if args.workload == HEADLINE and not args.k and args.shard == 1
+                                 else None),
                      "kernel": wk["kernel"]},
         "quantize": {"GB/s": round(bytes_q / tq / 1e9, 1),
                      "frac": round(bytes_q / tq / 1e9 / HBM_PEAK_GBS, 4),

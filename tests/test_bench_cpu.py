@@ -172,3 +172,13 @@ def test_event_stride_leaves_enough_samples():
     for steps, stride in ((1, 1), (20, 1), (31, 1), (32, 2), (50, 3), (128, 8), (200, 8), (5000, 8)):
         assert bench.event_stride(steps) == stride
         assert len(range(0, steps, stride)) >= min(steps, 16)
+
+
+@pytest.mark.parametrize("argv", [["--shard", "3"], ["--shard", "0"], ["--shard", "8", "--workload", "backward_dw_colwise"],
+                                  ["--shard", "8", "--workload", "forward_2d_transposed"]])
+def test_shard_must_be_a_column_split_into_multiples_of_32(argv):
+    """--shard S takes the first N/S rows of B: S must divide N into multiples of 32, and the workloads
+    whose B is not a plain [N, K] row block refuse it (before any GPU work)."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode != 0 and "--shard" in (r.stderr + r.stdout)
