@@ -541,7 +541,7 @@ def run_tiny(args):
                        "step_hip_graph_replay": round(wall_graph * 1e6, 2)},
         "roofline": {"bound": "mfma", "achieved": round(flops / tg / 1e12, 3), "peak": FP4_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(flops / tg / 1e12 / FP4_PEAK_TFLOPS, 6), "traffic": None,
-                     "note": "33.6 MFLOP on 256 x 256 outputs: one 256x256 tile, launch-latency bound"},
+                     "note": "33.6 MFLOP on 256 x 256 outputs: four 128x128 tiles, launch-latency bound"},
         "quantize": {"GB/s": round(qbytes / (tq + tt) / 1e9, 2), "frac": round(qbytes / (tq + tt) / 1e9 / HBM_PEAK_GBS, 6),
                      "us": round((tq + tt) * 1e6, 2), "bytes": qbytes},
         "checks": {"per_tensor_nonzero_codes": nonzero, "gemm_max_abs_err_vs_fp64_oracle": err},

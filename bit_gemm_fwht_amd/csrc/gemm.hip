@@ -3,9 +3,11 @@
 // Operands are K-contiguous: A [M, K] and B [N, K] as packed E2M1 (2 per byte) or E4M3 bytes,
 // with one E8M0 scale per row and 32-wide K group (B may instead carry one scale per 32 x 32
 // tile). The matrix core applies both scales itself, so the main loop is loads + MFMA only.
-// Two kernels: k_gemm_big (256 x 256 tiles, 32x32x64 MFMA, operands copied straight into LDS; the
-// path for M, N >= 256 and K a multiple of its stage depth) and k_gemm below (128 x 128 tiles,
-// 16x16x128 MFMA; every other shape, K any multiple of 32).
+// Three kernels: k_gemm_big (256 x 256 tiles, 32x32x64 MFMA, operands copied straight into LDS; the
+// path for M, N >= 256 and K a multiple of its stage depth), k_gemm_mid (the same with 128 x 128
+// tiles, two workgroups per CU, where 256 x 256 tiles would fill at most half the CUs) and k_gemm
+// below (128 x 128 tiles, 16x16x128 MFMA, operands staged through registers; every other shape, K
+// any multiple of 32).
 //
 // Lane layouts of the 16x16x128 scaled MFMA (established with one-hot probes on the hardware):
 //  - FP4: lane l supplies row l % 16 and the 32 K values [32 (l / 16), +32) as 16 contiguous
@@ -292,10 +294,14 @@ __global__ __launch_bounds__(NT) void k_gemm(GemmArgs g) {
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <bool FP8>
+// TS = 256: 8 waves of 128 x 64 (one workgroup per CU: two 68 KB stages); TS = 128: 4 waves of
+// 64 x 64 (two workgroups per CU: two 34 KB stages each), for grids of 256 x 256 tiles that would
+// leave most CUs idle.
+template <bool FP8, int TS = 256>
 struct Big {
-    static constexpr int TM = 256, TN = 256, NW = 8, NTH = 64 * NW;
-    static constexpr int WTM = 4, WTN = 2;            // 32x32 tiles per wave (M x N)
+    static constexpr int TM = TS, TN = TS, NW = TS == 256 ? 8 : 4, NTH = 64 * NW;
+    static constexpr int WTM = TS == 256 ? 4 : 2, WTN = 2;  // 32x32 tiles per wave (M x N)
+    static constexpr int WN = TN / (32 * WTN);        // waves along N
     // One stage covers 128 bytes of every row (full 128-byte cache lines): 256 K values of FP4
     // or 128 of FP8.
     static constexpr int KSTEP = FP8 ? 128 : 256;
@@ -385,19 +391,16 @@ __device__ __forceinline__ void big_tile_coords(int b, int ntm, int ntn, int& tm
     tn = (b % (GM * ntn)) / gs;
 }
 
-// One 256 x 256 tile of C (tile row tm, tile column tn) by the whole 512-thread workgroup, LDS
-// `smem` of Big<FP8>::NST stages; every thread must call it. Leaves the LDS free (every copy into
-// it has landed) but does not end with a barrier.
-// Epilogue of a 256 x 256 tile: the accumulators (lane layout of the 32x32x64 MFMA tiles of
-// big_tile) to C, and to C_q when FQ; uses the first 256 * 528 bytes of `smem`, which must be free
-// (no copy into it still in flight). Every thread of the workgroup must call it.
-template <bool FP8, int OUT, bool NVG, int FQ>
-__device__ __forceinline__ void big_epilogue(const GemmArgs& g, v16f (&acc)[Big<FP8>::WTN][Big<FP8>::WTM], int64_t m0,
-                                             int64_t n0, uint8_t* smem) {
-    using C = Big<FP8>;
+// Epilogue of a TS x TS tile: the accumulators (lane layout of the 32x32x64 MFMA tiles of
+// big_tile) to C, and to C_q when FQ (TS = 256 only); uses the first TS * 528 bytes of `smem`, which
+// must be free (no copy into it still in flight). Every thread of the workgroup must call it.
+template <bool FP8, int OUT, bool NVG, int FQ, int TS = 256>
+__device__ __forceinline__ void big_epilogue(const GemmArgs& g, v16f (&acc)[Big<FP8, TS>::WTN][Big<FP8, TS>::WTM],
+                                             int64_t m0, int64_t n0, uint8_t* smem) {
+    using C = Big<FP8, TS>;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / C::WN, wn = wave % C::WN;
     const int fr = lane & 31, fg = lane >> 5;
     // Epilogue, staged through LDS so that every global store writes whole 16-byte pieces of a
     // row and consecutive lanes cover consecutive bytes. Lane (fr, fg) holds, for 4-register group
@@ -406,7 +409,7 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& g, v16f (&acc)[Big<
     // (all 256 columns), fp32 output in two (pass p holds columns wn*64 + 32 p + [0, 32) of each
     // wave column wn, i.e. four 128-byte runs per row).
     constexpr int EP = 528;                       // staged row pitch (512 B + 16 B of padding)
-    static_assert(256 * EP <= C::NST * C::STAGE, "staging buffer exceeds the stage buffers");
+    static_assert(TS == 128 || 256 * EP <= C::NST * C::STAGE, "staging buffer exceeds the stage buffers");
     constexpr int PASSES = OUT == DT_F32 ? 2 : 1;
     float gscale = 1.0f;
     if constexpr (NVG) gscale = (*g.ga) * (*g.gb);
@@ -417,6 +420,61 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& g, v16f (&acc)[Big<
     const int64_t me0 = m0 + opaque_zero, ne0 = n0 + opaque_zero, ldc = g.ldc + opaque_zero;
     char* const cbase = reinterpret_cast<char*>(g.c) + opaque_zero;
     const int64_t Mx = g.M + opaque_zero, Nx = g.N + opaque_zero;
+    if constexpr (TS == 128) {
+        // 128 x 128 tile, plain output: one pass stages all 128 rows (128 fp32 or bf16 values per
+        // row), then each row goes out as 16 (bf16) or 32 (fp32) 16-byte pieces
+        static_assert(FQ == FQ_NONE, "the fused output quantize runs on 256 x 256 tiles");
+        static_assert(128 * EP <= C::NST * C::STAGE, "staging buffer exceeds the stage buffers");
+        constexpr int ESZ = OUT == DT_F32 ? 4 : 2;
+        const bool vec_ok = ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) && ((ldc * ESZ) % 16 == 0);
+        barrier_only();  // every wave is done reading the stage buffers
+#pragma unroll
+        for (int im = 0; im < C::WTM; ++im)
+#pragma unroll
+            for (int in = 0; in < C::WTN; ++in) {
+                const int row = wm * 32 * C::WTM + 32 * im + fr;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float v[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = NVG ? acc[in][im][4 * q + i] * gscale : acc[in][im][4 * q + i];
+                    const int col = wn * 32 * C::WTN + 32 * in + 8 * q + 4 * fg;
+                    if constexpr (OUT == DT_F32) {
+                        *reinterpret_cast<f32x4*>(smem + row * EP + 4 * col) = (f32x4){v[0], v[1], v[2], v[3]};
+                    } else {
+                        *reinterpret_cast<u32x2*>(smem + row * EP + 2 * col) =
+                            (u32x2){pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3])};
+                    }
+                }
+            }
+        wait_lgkm0();
+        barrier_only();
+        constexpr int EPC = 16 / ESZ;     // elements per 16-byte piece
+        constexpr int PPR = C::TN / EPC;  // pieces per row
+        const int c16 = tid % PPR;
+        const int64_t n = ne0 + EPC * c16;
+#pragma unroll 4
+        for (int r = tid / PPR; r < C::TM; r += C::NTH / PPR) {
+            const int64_t m = me0 + r;
+            if (m >= Mx) break;
+            const u32x4 val = *reinterpret_cast<const u32x4*>(smem + r * EP + 16 * c16);
+            char* cp = cbase + (m * ldc + n) * ESZ;
+            if (vec_ok && n + EPC <= Nx) {
+                *reinterpret_cast<u32x4*>(cp) = val;
+            } else {
+#pragma unroll
+                for (int i = 0; i < EPC; ++i) {
+                    if (n + i < Nx) {
+                        if constexpr (OUT == DT_F32)
+                            reinterpret_cast<uint32_t*>(cp)[i] = val[i];
+                        else
+                            reinterpret_cast<uint16_t*>(cp)[i] = (uint16_t)(val[i >> 1] >> (16 * (i & 1)));
+                    }
+                }
+            }
+        }
+        return;
+    }
     if constexpr (FQ != FQ_NONE) {
         // fused output quantization, in two passes of 128 columns: the fp32 values (as an fp32 C
         // would hold them) are staged in LDS, [256 rows][128] per pass (pass p holds tile columns
@@ -570,12 +628,15 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& g, v16f (&acc)[Big<
     }
 }
 
-template <bool FP8, bool B2D, int OUT, bool NVG, int FQ>
+// One TS x TS tile of C (tile row tm, tile column tn) by the whole workgroup (512 threads for
+// TS = 256, 256 for TS = 128), LDS `smem` of Big<FP8, TS>::NST stages; every thread must call it.
+// Leaves the LDS free (every copy into it has landed) but does not end with a barrier.
+template <bool FP8, bool B2D, int OUT, bool NVG, int FQ, int TS = 256>
 __device__ __forceinline__ void big_tile(const GemmArgs& g, int tm, int tn, uint8_t* smem) {
-    using C = Big<FP8>;
+    using C = Big<FP8, TS>;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / C::WN, wn = wave % C::WN;
     const int64_t m0 = (int64_t)tm * C::TM, n0 = (int64_t)tn * C::TN;
 
     const int64_t rowbytes = FP8 ? g.K : g.K / 2;
@@ -682,8 +743,8 @@ __device__ __forceinline__ void big_tile(const GemmArgs& g, int tm, int tn, uint
             const int c = FP8 ? (4 * kk + 2 * p + fg) : (2 * kk + fg);
             ch[kk][p] = 16 * (c ^ sw);
         }
-    const int aRow = C::OFF_A + (wm * 128 + fr) * C::RB, bRow = C::OFF_B + (wn * 64 + fr) * C::RB;
-    const int aScl = C::SPR * (wm * 128 + fr), bScl = C::OFF_SB + C::SPR * (wn * 64 + fr);
+    const int aRow = C::OFF_A + (wm * 32 * C::WTM + fr) * C::RB, bRow = C::OFF_B + (wn * 32 * C::WTN + fr) * C::RB;
+    const int aScl = C::SPR * (wm * 32 * C::WTM + fr), bScl = C::OFF_SB + C::SPR * (wn * 32 * C::WTN + fr);
     const int sshift = 8 * fg;
 
     issue(0);
@@ -767,7 +828,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& g, int tm, int tn, uint
     }
     wait_vm<0>();  // the dummy stage's zero-fill has landed before the LDS is reused
 
-    big_epilogue<FP8, OUT, NVG, FQ>(g, acc, m0, n0, smem);
+    big_epilogue<FP8, OUT, NVG, FQ, TS>(g, acc, m0, n0, smem);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -942,6 +1003,16 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
     int tm, tn;
     big_tile_coords(blockIdx.x, ntm, ntn, tm, tn);
     big_tile<FP8, B2D, OUT, NVG, FQ>(g, tm, tn, smem);
+}
+
+// 128 x 128 tiles of the same kernel, two workgroups per CU (plain output only)
+template <bool FP8, bool B2D, int OUT, bool NVG>
+__global__ __launch_bounds__(256, 2) void k_gemm_mid(GemmArgs g) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int ntm = (int)((g.M + 127) / 128), ntn = (int)((g.N + 127) / 128);
+    int tm, tn;
+    big_tile_coords(blockIdx.x, ntm, ntn, tm, tn);
+    big_tile<FP8, B2D, OUT, NVG, FQ_NONE, 128>(g, tm, tn, smem);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1129,11 +1200,46 @@ hipError_t launch_nv_to_fp8(const uint8_t* codes, const uint8_t* scales, int64_t
     return hipGetLastError();
 }
 
+// Compute units of the current device (looked up once per device).
+static hipError_t cu_count(int* n) {
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 64 && (*n = cus[dev].load(std::memory_order_acquire)) > 0) return hipSuccess;
+    e = hipDeviceGetAttribute(n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess && dev < 64) cus[dev].store(*n, std::memory_order_release);
+    return e;
+}
+
 template <bool FP8, bool B2D, bool NVG, int FQ>
 static hipError_t launch_out(const GemmArgs& g, int c_dtype, hipStream_t s) {
     const int64_t rowb = FP8 ? g.K : g.K / 2;
-    if (g.M >= 256 && g.N >= 256 && g.K % Big<FP8>::KSTEP == 0 && g.M * rowb < (1ll << 31) &&
-        g.N * rowb < (1ll << 31)) {
+    const bool direct = g.K % Big<FP8>::KSTEP == 0 && g.M * rowb < (1ll << 31) && g.N * rowb < (1ll << 31);
+    const int64_t big_tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
+    // 128 x 128 tiles where 256 x 256 ones would fill at most half the CUs (measured faster there:
+    // 64-128 such tiles on 256 CUs; slower from 176 on), for the plain output
+    if (FQ == FQ_NONE && direct && g.M >= 256 && g.N >= 256) {
+        int cus = 0;
+        const hipError_t e = cu_count(&cus);
+        if (e != hipSuccess) return e;
+        if (2 * big_tiles <= cus) {
+            using C = Big<FP8, 128>;
+            const unsigned tiles = (unsigned)(((g.M + 127) / 128) * ((g.N + 127) / 128));
+            const size_t lds = (size_t)C::NST * C::STAGE;
+            if (c_dtype == DT_BF16) {
+                hipError_t e2 = allow_lds<k_gemm_mid<FP8, B2D, DT_BF16, NVG>>(lds);
+                if (e2 != hipSuccess) return e2;
+                hipLaunchKernelGGL((k_gemm_mid<FP8, B2D, DT_BF16, NVG>), dim3(tiles), dim3(C::NTH), lds, s, g);
+            } else {
+                hipError_t e2 = allow_lds<k_gemm_mid<FP8, B2D, DT_F32, NVG>>(lds);
+                if (e2 != hipSuccess) return e2;
+                hipLaunchKernelGGL((k_gemm_mid<FP8, B2D, DT_F32, NVG>), dim3(tiles), dim3(C::NTH), lds, s, g);
+            }
+            return hipGetLastError();
+        }
+    }
+    if (g.M >= 256 && g.N >= 256 && direct) {
         using C = Big<FP8>;
         const unsigned tiles = (unsigned)(((g.M + 255) / 256) * ((g.N + 255) / 256));
         const size_t lds = (size_t)C::NST * C::STAGE;

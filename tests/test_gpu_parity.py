@@ -345,6 +345,42 @@ def test_gemm_k_not_a_multiple_of_128(orc, M, N, K, kind):
     _gemm_check(orc, A, B, pa, pb, c_dtype=torch.bfloat16)
 
 
+@pytest.mark.parametrize("kind", ["mxfp4", "mxfp4_2d", "mxfp8", "nvfp4"])
+@pytest.mark.parametrize("c_dtype", [torch.float32, torch.bfloat16])
+def test_gemm_128_tiles_equal_256_tiles(orc, kind, c_dtype):
+    """A product whose 256 x 256 tile grid would fill at most half the CUs runs on 128 x 128 tiles of
+    the same kernel (two workgroups per CU). Both accumulate every output over K in the same order,
+    so C from the 4096-row product (144 tiles of 256 x 256) and C from its first 512 rows alone
+    (18 such tiles, hence 128 x 128 tiles) agree bit for bit; the small launch also meets the
+    bound against the oracle."""
+    M, N, K = 4096, 2304, 512
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert 2 * 144 > cus >= 2 * 18, f"{cus} CUs: the two launches would not take different tile sizes"
+    rng = np.random.default_rng(41)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    if kind == "mxfp4":
+        pa, pb = P(), P(scale_mode=CEIL)
+    elif kind == "mxfp4_2d":
+        pa, pb = P(), P(block=(32, 32), scale_mode=CEIL)
+    elif kind == "mxfp8":
+        pa, pb = P(elem=E4M3), P(elem=E4M3, scale_mode=CEIL)
+    else:
+        pa, pb = P(block=(1, 16), scale_mode=NV46), P(block=(1, 16), scale_mode=NV)
+    qa = fp4.quantize(_to_dev(A), pa)
+    qb = fp4.quantize(_to_dev(B), pb)
+    c_full = fp4.gemm(qa, qb, out_dtype=c_dtype)
+    rows = 512
+    cb = fp4.buffer_sizes(rows, K, pa)
+    qa_top = fp4.QTensor(qa.codes[:cb[0]], qa.scales[:cb[1]], qa.tensor_scale, rows, K, pa)
+    c_top = fp4.gemm(qa_top, qb, out_dtype=c_dtype)
+    torch.cuda.synchronize()
+    iv = torch.int16 if c_dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(c_top.view(iv), c_full[:rows].view(iv))
+    _gemm_check(orc, A[:rows], B, pa, pb, c_dtype=c_dtype, sample=(np.random.default_rng(5).integers(0, rows, 4096),
+                                                                   np.random.default_rng(6).integers(0, N, 4096)))
+
+
 def test_nvfp4_gemm_without_workspace_needs_k_multiple_of_128():
     """The in-LDS re-expression runs 128-deep stages: with K % 128 != 0 an NVFP4 product needs the
     workspace, and the call says so before it launches anything."""
