@@ -5,9 +5,9 @@
 // tile). The matrix core applies both scales itself, so the main loop is loads + MFMA only.
 // Three kernels: k_gemm_big (256 x 256 tiles, 32x32x64 MFMA, operands copied straight into LDS; the
 // path for M, N >= 256 and K a multiple of its stage depth), k_gemm_mid (the same with 128 x 128
-// tiles, two workgroups per CU, where 256 x 256 tiles would fill at most half the CUs) and k_gemm
-// below (128 x 128 tiles, 16x16x128 MFMA, operands staged through registers; every other shape, K
-// any multiple of 32).
+// tiles, two workgroups per CU, for the plain output where M or N is below 256 or 256 x 256 tiles
+// would fill at most half the CUs) and k_gemm below (128 x 128 tiles, 16x16x128 MFMA, operands
+// staged through registers; every other shape, K any multiple of 32).
 //
 // Lane layouts of the 16x16x128 scaled MFMA (established with one-hot probes on the hardware):
 //  - FP4: lane l supplies row l % 16 and the 32 K values [32 (l / 16), +32) as 16 contiguous
@@ -1217,13 +1217,14 @@ static hipError_t launch_out(const GemmArgs& g, int c_dtype, hipStream_t s) {
     const int64_t rowb = FP8 ? g.K : g.K / 2;
     const bool direct = g.K % Big<FP8>::KSTEP == 0 && g.M * rowb < (1ll << 31) && g.N * rowb < (1ll << 31);
     const int64_t big_tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
-    // 128 x 128 tiles where 256 x 256 ones would fill at most half the CUs (measured faster there:
-    // 64-128 such tiles on 256 CUs; slower from 176 on), for the plain output
-    if (FQ == FQ_NONE && direct && g.M >= 256 && g.N >= 256) {
+    // 128 x 128 tiles, for the plain output, where 256 x 256 ones would fill at most half the CUs
+    // (measured faster there: 64-128 such tiles on 256 CUs; slower from 176 on) and where M or N is
+    // below 256 (faster than the register-staged kernel)
+    if (FQ == FQ_NONE && direct) {
         int cus = 0;
         const hipError_t e = cu_count(&cus);
         if (e != hipSuccess) return e;
-        if (2 * big_tiles <= cus) {
+        if (g.M < 256 || g.N < 256 || 2 * big_tiles <= cus) {
             using C = Big<FP8, 128>;
             const unsigned tiles = (unsigned)(((g.M + 127) / 128) * ((g.N + 127) / 128));
             const size_t lds = (size_t)C::NST * C::STAGE;

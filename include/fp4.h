@@ -208,9 +208,11 @@ int fp4_hadamard(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int
  * E8M0 (1, 32)), and NVFP4 x NVFP4 (E2M1, (1, 16) NV or 4/6 scales: each 32-wide K group is
  * re-expressed as E4M3 elements under one power-of-two scale and multiplied on the FP8 matrix
  * cores, and the product of the two tensor scales is applied in the epilogue).
- * K is a multiple of 32 (every operand layout requires it). The 256 x 256 tile kernels take
- * M, N >= 256 and K % 256 == 0 (MXFP4) or K % 128 == 0 (MXFP8, NVFP4); every other shape runs on
- * the 128 x 128 kernel, whose last 128-deep step may lie partly past K (it reads nothing there).
+ * K is a multiple of 32 (every operand layout requires it). Tiles: with K % 256 == 0 (MXFP4) or
+ * K % 128 == 0 (MXFP8, NVFP4), 256 x 256 where M, N >= 256 and the grid fills more than half the
+ * CUs (and always with the fused output quantize), else 128 x 128 on the same kernel; any other K
+ * runs on a 128 x 128 kernel whose last 128-deep step may lie partly past K (it reads nothing
+ * there). Every tiling accumulates each output over K in the same order.
  * Operands must not be rotated differently: a rotation along K cancels in A B^T
  * only when both were rotated with the same n, which the caller ensures.
  * Optional fused output quantization ("online quantization" of the output in the QuTLASS kernel

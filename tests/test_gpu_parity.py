@@ -351,8 +351,8 @@ def test_gemm_128_tiles_equal_256_tiles(orc, kind, c_dtype):
     """A product whose 256 x 256 tile grid would fill at most half the CUs runs on 128 x 128 tiles of
     the same kernel (two workgroups per CU). Both accumulate every output over K in the same order,
     so C from the 4096-row product (144 tiles of 256 x 256) and C from its first 512 rows alone
-    (18 such tiles, hence 128 x 128 tiles) agree bit for bit; the small launch also meets the
-    bound against the oracle."""
+    (18 such tiles, hence 128 x 128 tiles) agree bit for bit, and so does C from its first 200 rows
+    (M below 256); the 512-row launch also meets the bound against the oracle."""
     M, N, K = 4096, 2304, 512
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert 2 * 144 > cus >= 2 * 18, f"{cus} CUs: the two launches would not take different tile sizes"
@@ -370,13 +370,14 @@ def test_gemm_128_tiles_equal_256_tiles(orc, kind, c_dtype):
     qa = fp4.quantize(_to_dev(A), pa)
     qb = fp4.quantize(_to_dev(B), pb)
     c_full = fp4.gemm(qa, qb, out_dtype=c_dtype)
-    rows = 512
-    cb = fp4.buffer_sizes(rows, K, pa)
-    qa_top = fp4.QTensor(qa.codes[:cb[0]], qa.scales[:cb[1]], qa.tensor_scale, rows, K, pa)
-    c_top = fp4.gemm(qa_top, qb, out_dtype=c_dtype)
-    torch.cuda.synchronize()
     iv = torch.int16 if c_dtype == torch.bfloat16 else torch.int32
-    assert torch.equal(c_top.view(iv), c_full[:rows].view(iv))
+    for rows in (512, 200):  # 18 tiles of 256 x 256; M below 256 (both on 128 x 128 tiles)
+        cb = fp4.buffer_sizes(rows, K, pa)
+        qa_top = fp4.QTensor(qa.codes[:cb[0]], qa.scales[:cb[1]], qa.tensor_scale, rows, K, pa)
+        c_top = fp4.gemm(qa_top, qb, out_dtype=c_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(c_top.view(iv), c_full[:rows].view(iv)), f"first {rows} rows differ"
+    rows = 512
     _gemm_check(orc, A[:rows], B, pa, pb, c_dtype=c_dtype, sample=(np.random.default_rng(5).integers(0, rows, 4096),
                                                                    np.random.default_rng(6).integers(0, N, 4096)))
 
