@@ -649,9 +649,11 @@ def main():
         wk["K"] = args.k
     if args.shard != 1:
         n_s = wk["N"] // args.shard if args.shard > 1 else 0
-        if (args.workload in SHARD_EXCLUDED or n_s == 0 or wk["N"] % args.shard or n_s % 32):
+        unit = max(32, wk.get("out_q", {}).get("hadamard_n", 0))  # C's quantize groups / rotation chunks
+        if (args.workload in SHARD_EXCLUDED or n_s == 0 or wk["N"] % args.shard or n_s % unit):
             raise SystemExit(f"--shard {args.shard}: not a column-parallel split of {args.workload} "
-                             f"(N = {wk['N']} must split into multiples of 32; not for {sorted(SHARD_EXCLUDED)})")
+                             f"(N = {wk['N']} must split into multiples of {unit}; "
+                             f"not for {sorted(SHARD_EXCLUDED)})")
         wk["N"] = n_s
     M, N, K = wk["M"], wk["N"], wk["K"]
     pa, pb = params_of(fp4, wk["a"]), params_of(fp4, wk["b"])

@@ -5,8 +5,8 @@
 // tile). The matrix core applies both scales itself, so the main loop is loads + MFMA only.
 // Three kernels: k_gemm_big (256 x 256 tiles, 32x32x64 MFMA, operands copied straight into LDS; the
 // path for M, N >= 256 and K a multiple of its stage depth), k_gemm_mid (the same with 128 x 128
-// tiles, two workgroups per CU, for the plain output where M or N is below 256 or 256 x 256 tiles
-// would fill at most half the CUs) and k_gemm below (128 x 128 tiles, 16x16x128 MFMA, operands
+// tiles, two workgroups per CU, where M or N is below 256 or 256 x 256 tiles would fill at most
+// half the CUs; k_gemm_mid_q with the fused output quantize) and k_gemm below (128 x 128 tiles, 16x16x128 MFMA, operands
 // staged through registers; every other shape, K any multiple of 32).
 //
 // Lane layouts of the 16x16x128 scaled MFMA (established with one-hot probes on the hardware):
@@ -392,7 +392,7 @@ __device__ __forceinline__ void big_tile_coords(int b, int ntm, int ntn, int& tm
 }
 
 // Epilogue of a TS x TS tile: the accumulators (lane layout of the 32x32x64 MFMA tiles of
-// big_tile) to C, and to C_q when FQ (TS = 256 only); uses the first TS * 528 bytes of `smem`, which
+// big_tile) to C, and to C_q when FQ; uses the first TS * 528 bytes of `smem`, which
 // must be free (no copy into it still in flight). Every thread of the workgroup must call it.
 template <bool FP8, int OUT, bool NVG, int FQ, int TS = 256>
 __device__ __forceinline__ void big_epilogue(const GemmArgs& g, v16f (&acc)[Big<FP8, TS>::WTN][Big<FP8, TS>::WTM],
@@ -420,10 +420,9 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& g, v16f (&acc)[Big<
     const int64_t me0 = m0 + opaque_zero, ne0 = n0 + opaque_zero, ldc = g.ldc + opaque_zero;
     char* const cbase = reinterpret_cast<char*>(g.c) + opaque_zero;
     const int64_t Mx = g.M + opaque_zero, Nx = g.N + opaque_zero;
-    if constexpr (TS == 128) {
+    if constexpr (TS == 128 && FQ == FQ_NONE) {
         // 128 x 128 tile, plain output: one pass stages all 128 rows (128 fp32 or bf16 values per
         // row), then each row goes out as 16 (bf16) or 32 (fp32) 16-byte pieces
-        static_assert(FQ == FQ_NONE, "the fused output quantize runs on 256 x 256 tiles");
         static_assert(128 * EP <= C::NST * C::STAGE, "staging buffer exceeds the stage buffers");
         constexpr int ESZ = OUT == DT_F32 ? 4 : 2;
         const bool vec_ok = ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) && ((ldc * ESZ) % 16 == 0);
@@ -476,20 +475,22 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& g, v16f (&acc)[Big<
         return;
     }
     if constexpr (FQ != FQ_NONE) {
-        // fused output quantization, in two passes of 128 columns: the fp32 values (as an fp32 C
-        // would hold them) are staged in LDS, [256 rows][128] per pass (pass p holds tile columns
-        // [128 p, 128 p + 128), written by the four waves with wn / 2 = p), then one thread per
-        // 32-column group reads its group back, rotates it along N if asked (the four groups of a
-        // row are in consecutive lanes) and quantizes it with the rules of the quantize kernels
-        static_assert(C::WTN == 2 && C::NTH == 512, "two staged passes of 128 columns");
-        for (int p = 0; p < 2; ++p) {
+        // fused output quantization, in passes of 128 columns (two for 256 x 256 tiles, one for
+        // 128 x 128): the fp32 values (as an fp32 C would hold them) are staged in LDS, [TS rows][128]
+        // per pass (pass p holds tile columns [128 p, 128 p + 128), written by the waves whose 64
+        // columns lie there), then one thread per 32-column group reads its group back, rotates it
+        // along N if asked (the four groups of a row are in consecutive lanes) and quantizes it with
+        // the rules of the quantize kernels
+        static_assert(C::WTN == 2, "64 columns per wave");
+        static_assert(C::TM * EP <= C::NST * C::STAGE, "staging buffer exceeds the stage buffers");
+        for (int p = 0; p < C::TN / 128; ++p) {
             barrier_only();  // every wave is done with the stage buffers / the last pass
             if ((wn >> 1) == p) {  // wave-uniform
 #pragma unroll
                 for (int in = 0; in < C::WTN; ++in)
 #pragma unroll
                     for (int im = 0; im < C::WTM; ++im) {
-                        const int row = wm * 128 + 32 * im + fr;
+                        const int row = wm * 32 * C::WTM + 32 * im + fr;
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             f32x4 v;
@@ -502,7 +503,7 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& g, v16f (&acc)[Big<
             wait_lgkm0();
             barrier_only();
 #pragma unroll 1
-            for (int t = tid; t < 256 * 4; t += C::NTH) {  // two sweeps, every lane in both
+            for (int t = tid; t < C::TM * 4; t += C::NTH) {  // two sweeps, every lane in both
                 const int r = t >> 2, j = t & 3;  // row, staged group
                 const int64_t m = me0 + r, nb = ne0 + 128 * p + 32 * j;
                 float v[32];
@@ -541,7 +542,7 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& g, v16f (&acc)[Big<
                 constexpr int ESZ = OUT == DT_F32 ? 4 : 2, EPC = 16 / ESZ, PPR = 128 / EPC;
                 const bool vec_ok = ((reinterpret_cast<uintptr_t>(g.c) & 15) == 0) && ((ldc * ESZ) % 16 == 0);
 #pragma unroll 1
-                for (int t = tid; t < 256 * PPR; t += C::NTH) {
+                for (int t = tid; t < C::TM * PPR; t += C::NTH) {
                     const int r = t / PPR, c = (t % PPR) * EPC;
                     const int64_t m = me0 + r, n = ne0 + 128 * p + c;
                     if (m >= Mx) continue;
@@ -1005,7 +1006,8 @@ __global__ __launch_bounds__(512) void k_gemm_big(GemmArgs g) {
     big_tile<FP8, B2D, OUT, NVG, FQ>(g, tm, tn, smem);
 }
 
-// 128 x 128 tiles of the same kernel, two workgroups per CU (plain output only)
+// 128 x 128 tiles of the same kernel, two workgroups per CU: plain output, and with the fused
+// output quantize
 template <bool FP8, bool B2D, int OUT, bool NVG>
 __global__ __launch_bounds__(256, 2) void k_gemm_mid(GemmArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -1013,6 +1015,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mid(GemmArgs g) {
     int tm, tn;
     big_tile_coords(blockIdx.x, ntm, ntn, tm, tn);
     big_tile<FP8, B2D, OUT, NVG, FQ_NONE, 128>(g, tm, tn, smem);
+}
+
+template <bool FP8, bool B2D, int OUT, bool NVG, int FQ>
+__global__ __launch_bounds__(256, 2) void k_gemm_mid_q(GemmArgs g) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int ntm = (int)((g.M + 127) / 128), ntn = (int)((g.N + 127) / 128);
+    int tm, tn;
+    big_tile_coords(blockIdx.x, ntm, ntn, tm, tn);
+    big_tile<FP8, B2D, OUT, NVG, FQ, 128>(g, tm, tn, smem);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1217,10 +1228,10 @@ static hipError_t launch_out(const GemmArgs& g, int c_dtype, hipStream_t s) {
     const int64_t rowb = FP8 ? g.K : g.K / 2;
     const bool direct = g.K % Big<FP8>::KSTEP == 0 && g.M * rowb < (1ll << 31) && g.N * rowb < (1ll << 31);
     const int64_t big_tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
-    // 128 x 128 tiles, for the plain output, where 256 x 256 ones would fill at most half the CUs
-    // (measured faster there: 64-128 such tiles on 256 CUs; slower from 176 on) and where M or N is
-    // below 256 (faster than the register-staged kernel)
-    if (FQ == FQ_NONE && direct) {
+    // 128 x 128 tiles where 256 x 256 ones would fill at most half the CUs (measured faster there:
+    // 64-128 such tiles on 256 CUs; slower from 176 on) and where M or N is below 256 (faster than
+    // the register-staged kernel)
+    if (direct) {
         int cus = 0;
         const hipError_t e = cu_count(&cus);
         if (e != hipSuccess) return e;
@@ -1228,14 +1239,23 @@ static hipError_t launch_out(const GemmArgs& g, int c_dtype, hipStream_t s) {
             using C = Big<FP8, 128>;
             const unsigned tiles = (unsigned)(((g.M + 127) / 128) * ((g.N + 127) / 128));
             const size_t lds = (size_t)C::NST * C::STAGE;
-            if (c_dtype == DT_BF16) {
-                hipError_t e2 = allow_lds<k_gemm_mid<FP8, B2D, DT_BF16, NVG>>(lds);
-                if (e2 != hipSuccess) return e2;
-                hipLaunchKernelGGL((k_gemm_mid<FP8, B2D, DT_BF16, NVG>), dim3(tiles), dim3(C::NTH), lds, s, g);
+            hipError_t e2;
+            if constexpr (FQ == FQ_NONE) {
+                if (c_dtype == DT_BF16) {
+                    if ((e2 = allow_lds<k_gemm_mid<FP8, B2D, DT_BF16, NVG>>(lds)) != hipSuccess) return e2;
+                    hipLaunchKernelGGL((k_gemm_mid<FP8, B2D, DT_BF16, NVG>), dim3(tiles), dim3(C::NTH), lds, s, g);
+                } else {
+                    if ((e2 = allow_lds<k_gemm_mid<FP8, B2D, DT_F32, NVG>>(lds)) != hipSuccess) return e2;
+                    hipLaunchKernelGGL((k_gemm_mid<FP8, B2D, DT_F32, NVG>), dim3(tiles), dim3(C::NTH), lds, s, g);
+                }
             } else {
-                hipError_t e2 = allow_lds<k_gemm_mid<FP8, B2D, DT_F32, NVG>>(lds);
-                if (e2 != hipSuccess) return e2;
-                hipLaunchKernelGGL((k_gemm_mid<FP8, B2D, DT_F32, NVG>), dim3(tiles), dim3(C::NTH), lds, s, g);
+                if (c_dtype == DT_BF16) {
+                    if ((e2 = allow_lds<k_gemm_mid_q<FP8, B2D, DT_BF16, NVG, FQ>>(lds)) != hipSuccess) return e2;
+                    hipLaunchKernelGGL((k_gemm_mid_q<FP8, B2D, DT_BF16, NVG, FQ>), dim3(tiles), dim3(C::NTH), lds, s, g);
+                } else {
+                    if ((e2 = allow_lds<k_gemm_mid_q<FP8, B2D, DT_F32, NVG, FQ>>(lds)) != hipSuccess) return e2;
+                    hipLaunchKernelGGL((k_gemm_mid_q<FP8, B2D, DT_F32, NVG, FQ>), dim3(tiles), dim3(C::NTH), lds, s, g);
+                }
             }
             return hipGetLastError();
         }

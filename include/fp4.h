@@ -210,7 +210,7 @@ int fp4_hadamard(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int
  * cores, and the product of the two tensor scales is applied in the epilogue).
  * K is a multiple of 32 (every operand layout requires it). Tiles: with K % 256 == 0 (MXFP4) or
  * K % 128 == 0 (MXFP8, NVFP4), 256 x 256 where M, N >= 256 and the grid fills more than half the
- * CUs (and always with the fused output quantize), else 128 x 128 on the same kernel; any other K
+ * CUs, else 128 x 128 on the same kernel; any other K
  * runs on a 128 x 128 kernel whose last 128-deep step may lie partly past K (it reads nothing
  * there). Every tiling accumulates each output over K in the same order.
  * Operands must not be rotated differently: a rotation along K cancels in A B^T

@@ -175,6 +175,7 @@ def test_event_stride_leaves_enough_samples():
 
 
 @pytest.mark.parametrize("argv", [["--shard", "3"], ["--shard", "0"], ["--shard", "8", "--workload", "backward_dw_colwise"],
+                                  ["--shard", "4", "--workload", "llama7b_fused_out_q"],  # 2752 % 128 (C's H_128)
                                   ["--shard", "8", "--workload", "forward_2d_transposed"]])
 def test_shard_must_be_a_column_split_into_multiples_of_32(argv):
     """--shard S takes the first N/S rows of B: S must divide N into multiples of 32, and the workloads

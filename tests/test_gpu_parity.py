@@ -382,6 +382,36 @@ def test_gemm_128_tiles_equal_256_tiles(orc, kind, c_dtype):
                                                                    np.random.default_rng(6).integers(0, N, 4096)))
 
 
+@pytest.mark.parametrize("kind", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("oq_args", [dict(), dict(scale_mode=CEIL, round_mode=SR, seed=3, hadamard_n=128),
+                                     dict(elem=E4M3, hadamard_n=32)], ids=["e2m1", "e2m1_sr_h128", "e4m3_h32"])
+def test_fused_output_quantize_128_tiles_equal_256_tiles(kind, oq_args):
+    """The fused output quantize on 128 x 128 tiles (the first 512 or 200 rows of A alone) writes
+    the same C and C_q bytes as on 256 x 256 tiles (the 4096-row product): the quantization of a
+    row of C depends on that row only, stochastic rounding included (keyed by m * N + n)."""
+    M, N, K = 4096, 2304, 512
+    rng = np.random.default_rng(43)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    if kind == "mxfp4":
+        pa, pb = P(), P(scale_mode=CEIL)
+    else:
+        pa, pb = P(block=(1, 16), scale_mode=NV46), P(block=(1, 16), scale_mode=NV)
+    oq = P(**oq_args)
+    qa = fp4.quantize(_to_dev(A), pa)
+    qb = fp4.quantize(_to_dev(B), pb)
+    c_full, q_full = fp4.gemm(qa, qb, out_dtype=torch.float32, out_q=oq)
+    for rows in (512, 200):
+        cb = fp4.buffer_sizes(rows, K, pa)
+        qa_top = fp4.QTensor(qa.codes[:cb[0]], qa.scales[:cb[1]], qa.tensor_scale, rows, K, pa)
+        c_top, q_top = fp4.gemm(qa_top, qb, out_dtype=torch.float32, out_q=oq)
+        torch.cuda.synchronize()
+        qc, qs = fp4.buffer_sizes(rows, N, oq)[:2]
+        assert torch.equal(c_top.view(torch.int32), c_full[:rows].view(torch.int32)), f"C, first {rows} rows"
+        assert torch.equal(q_top.codes, q_full.codes[:qc]), f"C_q codes, first {rows} rows"
+        assert torch.equal(q_top.scales, q_full.scales[:qs]), f"C_q scales, first {rows} rows"
+
+
 def test_nvfp4_gemm_without_workspace_needs_k_multiple_of_128():
     """The in-LDS re-expression runs 128-deep stages: with K % 128 != 0 an NVFP4 product needs the
     workspace, and the call says so before it launches anything."""
