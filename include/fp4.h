@@ -21,8 +21,10 @@
  *    (memory of the current HIP device); fp4_qparams / fp4_qtensor structs are HOST pointers.
  *  - The caller owns every buffer and keeps it alive until the work queued on `stream` (a
  *    hipStream_t, or NULL for the default stream) has completed. The library allocates nothing,
- *    keeps no pointer after returning and holds no mutable global state: calls on different
- *    streams may run concurrently.
+ *    keeps no pointer after returning and holds no mutable global state beyond write-once facts
+ *    per device (its CU count, which kernels have had their LDS limit raised; both thread-safe)
+ *    and the allocation-free quantize's scratch below: calls on different streams may run
+ *    concurrently.
  *  - All work is queued asynchronously on `stream`; a return of FP4_OK means "queued".
  *  - Every argument is validated on the host before anything is queued. On any error nothing is
  *    queued and the outputs are left untouched. A launch failure returns FP4_ERR_HIP; a device
