@@ -693,7 +693,9 @@ def test_nvfp4_given_tensor_scale_parity(orc, mode, gfac, hn, rnd):
         assert np.all(np.abs(c.cpu().numpy() - ref) <= tol)
 
 
-@pytest.mark.parametrize("M,N,K", [(512, 768, 1024), (300, 544, 640), (200, 160, 384)])
+# (4096, 2304, 256): 144 tiles of 256 x 256 (more than half the CUs fill: the 256 x 256 kernel);
+# (512, 768, 1024) and (300, 544, 640) NVFP4: 128 x 128 tiles; the others the register-staged kernel
+@pytest.mark.parametrize("M,N,K", [(4096, 2304, 256), (512, 768, 1024), (300, 544, 640), (200, 160, 384)])
 @pytest.mark.parametrize("kind", ["mxfp4", "nvfp4"])
 @pytest.mark.parametrize("c_dtype", [torch.bfloat16, torch.float32])
 def test_gemm_into_a_column_block(M, N, K, kind, c_dtype):
