@@ -18,7 +18,7 @@ DEV = "cuda:0"
 
 pytestmark = pytest.mark.gpu
 
-N_QUANT, N_GEMM, N_EXTRA = 40, 24, 16
+N_QUANT, N_GEMM, N_EXTRA, N_TILES = 40, 24, 16, 24
 
 
 def _quant_case(seed):
@@ -80,6 +80,55 @@ def test_random_gemm(orc, seed):
     A = (rng.standard_normal((M, K)) * 10.0 ** rng.uniform(-2, 2)).astype(np.float32)
     B = (rng.standard_normal((N, K)) * 10.0 ** rng.uniform(-3, 1)).astype(np.float32)
     _gemm_check(orc, A, B, pa, pb, c_dtype=c_dtype)
+
+
+def _tile_case(seed):
+    """Shapes around the tile-size choices: M or N below 256, the 128 / 256 boundaries, grids of
+    256 x 256 tiles on either side of half the CU count, ragged edges, K from one stage to many, with
+    the plain output or the fused output quantize."""
+    rng = np.random.default_rng(3000 + seed)
+    kind = rng.choice(["mxfp4", "mxfp4_2d", "mxfp8", "nvfp4"])
+    M = int(rng.choice([int(rng.integers(1, 129)), int(rng.integers(120, 264)), int(rng.integers(250, 1400)),
+                        int(rng.integers(2600, 4200))]))
+    N = 32 * int(rng.choice([int(rng.integers(1, 9)), int(rng.integers(7, 10)), int(rng.integers(8, 45)),
+                             int(rng.integers(80, 131))]))
+    K = int(rng.choice([256, 512, 768, 1024, 2048, 4096]))
+    if kind == "mxfp4":
+        pa, pb = P(scale_mode=CEIL), P()
+    elif kind == "mxfp4_2d":
+        pa, pb = P(), P(block=(32, 32), scale_mode=CEIL)
+    elif kind == "mxfp8":
+        pa, pb = P(elem=E4M3), P(elem=E4M3, scale_mode=CEIL)
+        K = int(rng.choice([128, 384, 640, 1024, 2048]))
+    else:
+        pa, pb = P(block=(1, 16), scale_mode=NV46), P(block=(1, 16), scale_mode=NV)
+        K = int(rng.choice([128, 384, 640, 1024, 2048]))
+    c_dtype = torch.bfloat16 if rng.random() < 0.5 else torch.float32
+    out_q = None
+    if rng.random() < 0.35:
+        hn = int(rng.choice([h for h in (0, 32, 128) if N % max(h, 32) == 0]))
+        out_q = P(elem=E2M1 if rng.random() < 0.7 else E4M3, scale_mode=FLOOR if rng.random() < 0.5 else CEIL,
+                  round_mode=SR if rng.random() < 0.4 else RNE, hadamard_n=hn, seed=int(rng.integers(0, 2**40)))
+    return M, N, K, pa, pb, c_dtype, out_q
+
+
+@pytest.mark.parametrize("seed", range(N_TILES))
+def test_random_gemm_tile_choices(orc, seed):
+    """C within the GEMM bound on 4096 sampled outputs; with the fused output quantize, C_q equal to
+    the oracle's quantization of the same call's fp32 C, byte for byte."""
+    M, N, K, pa, pb, c_dtype, out_q = _tile_case(seed)
+    rng = np.random.default_rng(seed)
+    A = (rng.standard_normal((M, K)) * 10.0 ** rng.uniform(-1, 1)).astype(np.float32)
+    B = (rng.standard_normal((N, K)) * 10.0 ** rng.uniform(-2, 0)).astype(np.float32)
+    ms, ns = rng.integers(0, M, 4096), rng.integers(0, N, 4096)
+    _gemm_check(orc, A, B, pa, pb, c_dtype=c_dtype, sample=(ms, ns))
+    if out_q is not None:
+        qa, qb = fp4.quantize(_to_dev(A), pa), fp4.quantize(_to_dev(B), pb)
+        c, cq = fp4.gemm(qa, qb, out_dtype=torch.float32, out_q=out_q)
+        torch.cuda.synchronize()
+        oc, os_, _ = _orc_quant(orc, c.cpu().numpy(), out_q)
+        assert np.array_equal(cq.codes.cpu().numpy(), oc.reshape(-1)), f"C_q codes ({M}, {N}, {K})"
+        assert np.array_equal(cq.scales.cpu().numpy(), os_.reshape(-1).view(np.uint8)), f"C_q scales ({M}, {N}, {K})"
 
 
 def _input(rng, rows, cols, dtype):
